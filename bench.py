@@ -1,0 +1,181 @@
+"""Benchmark of the routed-MoE layer (Gemma 4 26B-A4B shape, Q4_0 experts) on one MI355X.
+
+One step = one pass of the whole layer (router + top-K, permutation, expert
+FFN, combine) over one batch of synthetic tokens.  Default workload: 1-token
+decode (H 2816, 128 experts, top-8, I 704, fp32 activations).  Inputs are
+resident in HBM before timing.  To keep the 256 MB Infinity Cache from
+serving the expert weights, steps rotate over several independently seeded
+weight sets (as consecutive layers of a model would).
+
+Prints one JSON line with the metric, the roofline of the dominant kernel
+(the expert FFN call) measured with HIP events on the launch stream, and the
+single-threaded CPU oracle's rate on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "MoE-layer tokens/sec at 1 MI355X; decode HBM GB/s %peak, prefill MFMA %peak"
+Q4_0_EXPERT_BYTES = lambda H, I: 3 * H * I // 32 * 18   # [gate; up] + down
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", type=int, default=1, help="workload index (1: decode 1 token)")
+    p.add_argument("--sets", type=int, default=0, help="weight sets rotated (0: auto)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def cpu_baseline(spec, seconds: float):
+    """The oracle as it stands, single-threaded, on a bounded token sample."""
+    import oracle
+    from sparse_moe_amd import synth
+    L = synth.make_layer(spec, T=1)
+    xs = synth.activations(spec, 64, spec.seed + 77)
+    n, t0 = 0, time.perf_counter()
+    while n < xs.shape[0]:
+        oracle.moe_layer(xs[n:n + 1], L.w_router, L.w_gate_up, L.w_down, spec.K,
+                         scale=L.expert_scale, bias=L.router_bias)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%d tokens of the %s layer, one at a time, full layer per token "
+                      "(router over all experts, top-%d, %d expert FFNs, combine), "
+                      "single-threaded binary64 C oracle" % (n, spec.name, spec.K, spec.K)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the layer would shard over experts)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sparse_moe_amd import binding, synth
+    torch.cuda.set_device(0)
+    spec = synth.SPECS[args.config]
+    T, H, E, K, I = spec.T, spec.H, spec.E, spec.K, spec.I
+    act = torch.float32 if spec.act == "f32" else torch.bfloat16
+    dev = "cuda"
+
+    def dev_t(a):
+        import numpy as np
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    expert_bytes = Q4_0_EXPERT_BYTES(H, I)
+    layer_bytes = E * expert_bytes
+    nsets = args.sets or max(1, min(16, -(-3 * 1024 ** 3 // layer_bytes)))
+    sets = []
+    for r in range(nsets):
+        L = synth.make_layer(spec, seed=spec.seed + 1000 * r, with_x=False)
+        sets.append(dict(wr=dev_t(L.w_router), gu=dev_t(L.w_gate_up), dn=dev_t(L.w_down),
+                         sc=dev_t(L.expert_scale),
+                         bias=None if L.router_bias is None else dev_t(L.router_bias)))
+        del L
+    npool = 16
+    xpool = dev_t(synth.activations(spec, T * npool, spec.seed + 7)).view(npool, T, H)
+    bufs = binding.LayerBuffers(T, H, I, E, K, act)
+
+    def step(i, ev_a=None, ev_b=None):
+        s = sets[i % nsets]
+        x = xpool[i % npool]
+        binding.moe_router_topk(x, s["wr"], bufs.logits, bufs.topk_ids, bufs.topk_w,
+                                logit_bias=s["bias"])
+        binding.moe_permute(bufs.topk_ids, E, bufs.offsets, bufs.sorted_slots, bufs.slot_pos,
+                            bufs.ws_perm)
+        if ev_a is not None:
+            ev_a.record()
+        binding.moe_expert_ffn_q4_0(x, s["gu"], s["dn"], K, bufs.offsets, bufs.sorted_slots,
+                                    bufs.y_sorted, bufs.ws_ffn)
+        if ev_b is not None:
+            ev_b.record()
+        binding.moe_combine(bufs.y_sorted, bufs.slot_pos, bufs.topk_ids, bufs.topk_w, s["sc"],
+                            out_f32=bufs.out)
+
+    # distinct experts per step (for the algorithmic bytes of the FFN)
+    distinct = []
+    for i in range(nsets):
+        step(i)
+        torch.cuda.synchronize()
+        distinct.append(int((bufs.offsets[1:] - bufs.offsets[:-1] > 0).sum().item()))
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(i, ev_a[i], ev_b[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    ffn_ms = [a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]
+    ffn_avg_ms = sum(ffn_ms) / len(ffn_ms)
+
+    # algorithmic bytes of one expert-FFN call (dominant kernel), averaged over the
+    # steps' distinct-expert counts
+    asz = 4 if act == torch.float32 else 2
+    N = T * K
+    d_avg = sum(distinct[i % nsets] for i in range(args.steps)) / args.steps
+    ffn_bytes = (d_avg * expert_bytes + T * H * asz + N * I * asz * 2 + N * H * 4)
+    achieved = ffn_bytes / (ffn_avg_ms * 1e-3) / 1e9
+    layer_hbm = (d_avg * expert_bytes + E * H * 4 + T * H * asz + E * 4 + T * H * 4) / (ms_step * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": T * args.steps / (ms_total * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4_0 x %s (int4 digit products, fp32 accumulate)" % spec.act,
+        "data": "synthetic (seeded; random-init Q4_0 experts, %d weight sets rotated)" % nsets,
+        "config": {"workload": "%s: Gemma-4-26B-A4B-shaped routed-MoE layer, T=%d, H=%d, E=%d, "
+                               "top-%d, I=%d, Q4_0 experts, %s activations"
+                               % (spec.name, T, H, E, K, I, spec.act),
+                   "tokens_per_step": T, "weight_sets": nsets,
+                   "distinct_experts_per_step": d_avg,
+                   "layer_hbm_gbs": layer_hbm, "layer_hbm_frac": layer_hbm / HBM_PEAK_GBS,
+                   "wall_s": wall},
+        "roofline": {"kernel": "moe_expert_ffn_q4_0 (gate/up + down Q4_0 GEMV)",
+                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": ffn_bytes, "avg_launch_us": ffn_avg_ms * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(spec, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

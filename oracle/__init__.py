@@ -52,6 +52,7 @@ def lib() -> C.CDLL:
         L.orc_gelu_tanh.argtypes = [d]; L.orc_gelu_tanh.restype = d
         L.orc_router_logits.argtypes = [p, i32, i64, i32, p, p, p, i32, p]
         L.orc_topk_softmax.argtypes = [p, i64, i32, i32, p, p]
+        L.orc_topk_weights.argtypes = [p, i64, i32, i32, p, p]
         L.orc_permute.argtypes = [p, i64, i32, i32, p, p, p]
         L.orc_expert_ffn_token.argtypes = [p, i32, i32, p, p, i32, i32, p, p]
         L.orc_expert_ffn.argtypes = [p, i32, i64, i32, p, p, i32, i32, i32, p, p, p, p]
@@ -59,7 +60,7 @@ def lib() -> C.CDLL:
         L.orc_rmsnorm.argtypes = [p, i32, p, d, i64, i32, p]
         L.orc_moe_layer.argtypes = [p, i32, i64, i32, p, p, p, p, i32, i32, p, p, i32, p, p,
                                     p, p, p, p, p, p, p]
-        for f in ("orc_router_logits", "orc_topk_softmax", "orc_permute", "orc_expert_ffn_token",
+        for f in ("orc_router_logits", "orc_topk_softmax", "orc_topk_weights", "orc_permute", "orc_expert_ffn_token",
                   "orc_expert_ffn", "orc_combine", "orc_rmsnorm", "orc_moe_layer"):
             getattr(L, f).restype = i32
         _lib = L
@@ -133,6 +134,16 @@ def topk_softmax(logits: np.ndarray, K: int):
     w = np.empty((T, K), np.float64)
     _check(lib().orc_topk_softmax(_ptr(l), T, E, K, _ptr(ids), _ptr(w)), "orc_topk_softmax")
     return ids, w
+
+
+def topk_weights(logits: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    l = np.ascontiguousarray(logits, np.float64)
+    ids = np.ascontiguousarray(ids, np.int32)
+    T, E = l.shape
+    K = ids.shape[1]
+    w = np.empty((T, K), np.float64)
+    _check(lib().orc_topk_weights(_ptr(l), T, E, K, _ptr(ids), _ptr(w)), "orc_topk_weights")
+    return w
 
 
 def permute(ids: np.ndarray, E: int):

@@ -120,13 +120,33 @@ int orc_router_logits(const void* x, int x_dt, int64_t T, int H, const float* w_
     return 0;
 }
 
+/* Renormalised softmax weights of given experts: p = softmax over all E
+ * logits, w[t,k] = p[ids[t,k]] / sum_k p[ids[t,k]]. */
+int orc_topk_weights(const double* logits, int64_t T, int E, int K, const int32_t* ids, double* w) {
+    if (T < 0 || E <= 0 || K <= 0 || K > E || !logits || !ids || !w) return 1;
+    double* p = (double*)malloc(sizeof(double) * (size_t)E);
+    if (!p) return 2;
+    for (int64_t t = 0; t < T; ++t) {
+        const double* l = logits + t * E;
+        double mx = l[0];
+        for (int e = 1; e < E; ++e) if (l[e] > mx) mx = l[e];
+        double z = 0.0;
+        for (int e = 0; e < E; ++e) { p[e] = exp(l[e] - mx); z += p[e]; }
+        for (int e = 0; e < E; ++e) p[e] /= z;
+        double s = 0.0;
+        for (int k = 0; k < K; ++k) s += p[ids[t * K + k]];
+        for (int k = 0; k < K; ++k) w[t * K + k] = p[ids[t * K + k]] / s;
+    }
+    free(p);
+    return 0;
+}
+
 /* Stable insertion sort of expert indices by descending logit: equal logits
- * keep ascending expert order. */
+ * keep ascending expert order; the first K are the chosen experts. */
 int orc_topk_softmax(const double* logits, int64_t T, int E, int K, int32_t* ids, double* w) {
     if (T < 0 || E <= 0 || K <= 0 || K > E || !logits || !ids || !w) return 1;
     int* order = (int*)malloc(sizeof(int) * (size_t)E);
-    double* p = (double*)malloc(sizeof(double) * (size_t)E);
-    if (!order || !p) { free(order); free(p); return 2; }
+    if (!order) return 2;
     for (int64_t t = 0; t < T; ++t) {
         const double* l = logits + t * E;
         for (int e = 0; e < E; ++e) {
@@ -134,23 +154,10 @@ int orc_topk_softmax(const double* logits, int64_t T, int E, int K, int32_t* ids
             while (i > 0 && l[order[i - 1]] < l[e]) { order[i] = order[i - 1]; --i; }
             order[i] = e;
         }
-        /* softmax over all experts */
-        double mx = l[0];
-        for (int e = 1; e < E; ++e) if (l[e] > mx) mx = l[e];
-        double z = 0.0;
-        for (int e = 0; e < E; ++e) { p[e] = exp(l[e] - mx); z += p[e]; }
-        for (int e = 0; e < E; ++e) p[e] /= z;
-        /* keep the K largest, renormalise their probabilities */
-        double s = 0.0;
-        for (int k = 0; k < K; ++k) s += p[order[k]];
-        for (int k = 0; k < K; ++k) {
-            ids[t * K + k] = order[k];
-            w[t * K + k] = p[order[k]] / s;
-        }
+        for (int k = 0; k < K; ++k) ids[t * K + k] = order[k];
     }
     free(order);
-    free(p);
-    return 0;
+    return orc_topk_weights(logits, T, E, K, ids, w);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -61,6 +61,9 @@ int orc_router_logits(const void* x, int x_dt, int64_t T, int H, const float* w_
  * lower expert first); p = softmax over all E; w[t,k] = p[ids[t,k]] / sum_k p[ids[t,k]]. */
 int orc_topk_softmax(const double* logits, int64_t T, int E, int K, int32_t* ids, double* w);
 
+/* The weights alone, for given expert ids (the second half of orc_topk_softmax). */
+int orc_topk_weights(const double* logits, int64_t T, int E, int K, const int32_t* ids, double* w);
+
 /* Stable counting sort of slots s = t*K + k by ids[s]: offsets[E+1] exclusive
  * prefix of per-expert counts, sorted_slots[p] = slot at position p,
  * slot_pos[s] = position of slot s. */

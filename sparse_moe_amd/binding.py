@@ -1,0 +1,240 @@
+"""ctypes binding of libsparse_moe_amd.so (the C ABI in include/sparse_moe.h).
+
+Argument marshalling only: each function checks dtypes, shapes, contiguity and
+device of its torch tensors, then passes raw device pointers, sizes and the
+current torch stream to the C entry point of the same name.  Every step of the
+layer runs in the library's HIP kernels; there is no fallback.  If the library
+is missing the import of this module fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch  # must be imported before the library so both share one HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsparse_moe_amd.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_MAX_E, MOE_MAX_K = 256, 16
+
+_STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN",
+           4: "MOE_ERR_UNSUPPORTED", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_HIP"}
+
+# every function the header declares, with its ctypes signature
+_P, _I32, _I64, _SZ, _F32 = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_float
+SIGNATURES = {
+    "moe_status_string": ([C.c_int], C.c_char_p),
+    "moe_abi_version": ([], C.c_int),
+    "moe_router_topk": ([_P, C.c_int, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _P, _P, _P], C.c_int),
+    "moe_permute_workspace_bytes": ([_I64, _I32, _I32], _SZ),
+    "moe_permute": ([_P, _I64, _I32, _I32, _P, _P, _P, _P, _SZ, _P], C.c_int),
+    "moe_expert_ffn_q4_0_workspace_bytes": ([_I64, _I32, _I32, _I32, _I32, C.c_int], _SZ),
+    "moe_expert_ffn_q4_0": ([_P, C.c_int, _I64, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P,
+                             _SZ, _P], C.c_int),
+    "moe_combine": ([_P, _P, _P, _P, _P, _I64, _I32, _I32, _P, C.c_int, _P, _P, C.c_int, _P],
+                    C.c_int),
+    "moe_rmsnorm": ([_P, C.c_int, _P, _F32, _I64, _I32, _P, C.c_int, _P], C.c_int),
+}
+
+
+class MoEError(RuntimeError):
+    pass
+
+
+def _load() -> C.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libsparse_moe_amd.so is not built (expected at %s); run "
+                          "`python -m sparse_moe_amd.build`" % LIB_PATH)
+    L = C.CDLL(LIB_PATH)
+    for name, (args, res) in SIGNATURES.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    return L
+
+
+lib = _load()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise MoEError("%s: %s (%s)" % (what, _STATUS.get(rc, rc),
+                                        lib.moe_status_string(rc).decode()))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def act_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError("activations must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+# ---- the four calls of a layer ----------------------------------------------------
+def moe_router_topk(x: Optional[torch.Tensor], W_r: Optional[torch.Tensor], logits: torch.Tensor,
+                    topk_ids: torch.Tensor, topk_w: torch.Tensor, r_scale=None, logit_bias=None,
+                    stream=None):
+    """x [T,H] f32/bf16, W_r [E,H] f32 (None: logits [T,E] are an input)."""
+    T, E = logits.shape
+    K = topk_ids.shape[1]
+    H = 0 if W_r is None else W_r.shape[1]
+    for t, n, d in ((x, "x", None), (W_r, "W_r", torch.float32), (logits, "logits", torch.float32),
+                    (topk_ids, "topk_ids", torch.int32), (topk_w, "topk_w", torch.float32),
+                    (r_scale, "r_scale", torch.float32), (logit_bias, "logit_bias", torch.float32)):
+        _dev(t, n, d)
+    if W_r is not None and (x is None or tuple(x.shape) != (T, H) or W_r.shape[0] != E):
+        raise ValueError("router shapes disagree")
+    if tuple(topk_w.shape) != (T, K):
+        raise ValueError("topk_w must be [T, K]")
+    xdt = act_dtype(x) if x is not None else MOE_F32
+    _check(lib.moe_router_topk(_ptr(x), xdt, T, H, _ptr(W_r), _ptr(r_scale), _ptr(logit_bias), E, K,
+                               _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _stream(stream)),
+           "moe_router_topk")
+
+
+def moe_permute_workspace_bytes(T: int, K: int, E: int) -> int:
+    return lib.moe_permute_workspace_bytes(T, K, E)
+
+
+def moe_permute(topk_ids: torch.Tensor, E: int, expert_offsets: torch.Tensor,
+                sorted_slots: torch.Tensor, slot_pos: torch.Tensor,
+                ws: Optional[torch.Tensor] = None, stream=None):
+    T, K = topk_ids.shape
+    for t, n in ((topk_ids, "topk_ids"), (expert_offsets, "expert_offsets"),
+                 (sorted_slots, "sorted_slots"), (slot_pos, "slot_pos")):
+        _dev(t, n, torch.int32)
+    _dev(ws, "ws")
+    if expert_offsets.numel() != E + 1 or sorted_slots.numel() != T * K or slot_pos.numel() != T * K:
+        raise ValueError("permutation output sizes disagree")
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.moe_permute(_ptr(topk_ids), T, K, E, _ptr(expert_offsets), _ptr(sorted_slots),
+                           _ptr(slot_pos), _ptr(ws), nbytes, _stream(stream)), "moe_permute")
+
+
+def moe_expert_ffn_q4_0_workspace_bytes(T: int, K: int, H: int, I: int, E: int, x_dt: int) -> int:
+    return lib.moe_expert_ffn_q4_0_workspace_bytes(T, K, H, I, E, x_dt)
+
+
+def moe_expert_ffn_q4_0(x: torch.Tensor, w_gate_up: torch.Tensor, w_down: torch.Tensor, K: int,
+                        expert_offsets: torch.Tensor, sorted_slots: torch.Tensor,
+                        y_sorted: torch.Tensor, ws: torch.Tensor, stream=None):
+    """w_gate_up uint8 [E, 2I, H/32, 18], w_down uint8 [E, H, I/32, 18] (raw Q4_0 bytes)."""
+    T, H = x.shape
+    E = w_gate_up.shape[0]
+    I = w_gate_up.shape[1] // 2
+    _dev(x, "x")
+    _dev(w_gate_up, "w_gate_up", torch.uint8)
+    _dev(w_down, "w_down", torch.uint8)
+    _dev(expert_offsets, "expert_offsets", torch.int32)
+    _dev(sorted_slots, "sorted_slots", torch.int32)
+    _dev(y_sorted, "y_sorted", torch.float32)
+    _dev(ws, "ws")
+    if w_gate_up.numel() != E * 2 * I * (H // 32) * 18 or w_down.numel() != E * H * (I // 32) * 18:
+        raise ValueError("Q4_0 weight sizes disagree with [E][2I][H/32][18] / [E][H][I/32][18]")
+    if tuple(y_sorted.shape) != (T * K, H):
+        raise ValueError("y_sorted must be [T*K, H]")
+    _check(lib.moe_expert_ffn_q4_0(_ptr(x), act_dtype(x), T, H, _ptr(w_gate_up), _ptr(w_down), I, E,
+                                   K, _ptr(expert_offsets), _ptr(sorted_slots), _ptr(y_sorted),
+                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_expert_ffn_q4_0")
+
+
+def moe_combine(y_sorted: torch.Tensor, slot_pos: torch.Tensor, topk_ids: torch.Tensor,
+                topk_w: torch.Tensor, expert_scale: Optional[torch.Tensor] = None,
+                out_f32: Optional[torch.Tensor] = None, out_act: Optional[torch.Tensor] = None,
+                residual: Optional[torch.Tensor] = None, stream=None):
+    T, K = topk_w.shape
+    H = y_sorted.shape[1]
+    _dev(y_sorted, "y_sorted", torch.float32)
+    _dev(slot_pos, "slot_pos", torch.int32)
+    _dev(topk_ids, "topk_ids", torch.int32)
+    _dev(topk_w, "topk_w", torch.float32)
+    _dev(expert_scale, "expert_scale", torch.float32)
+    _dev(out_f32, "out_f32", torch.float32)
+    _dev(out_act, "out_act")
+    _dev(residual, "residual")
+    rdt = act_dtype(residual) if residual is not None else MOE_F32
+    odt = act_dtype(out_act) if out_act is not None else MOE_F32
+    _check(lib.moe_combine(_ptr(y_sorted), _ptr(slot_pos), _ptr(topk_ids), _ptr(topk_w),
+                           _ptr(expert_scale), T, K, H, _ptr(residual), rdt, _ptr(out_f32),
+                           _ptr(out_act), odt, _stream(stream)), "moe_combine")
+
+
+def moe_rmsnorm(x: torch.Tensor, w: torch.Tensor, eps: float, out: torch.Tensor, stream=None):
+    T, H = x.shape
+    _dev(x, "x")
+    _dev(w, "w", torch.float32)
+    _dev(out, "out")
+    _check(lib.moe_rmsnorm(_ptr(x), act_dtype(x), _ptr(w), eps, T, H, _ptr(out), act_dtype(out),
+                           _stream(stream)), "moe_rmsnorm")
+
+
+# ---- buffers of one layer and the four calls in order -------------------------------
+class LayerBuffers:
+    """Device buffers for one layer of T tokens (torch allocates them)."""
+
+    def __init__(self, T: int, H: int, I: int, E: int, K: int, act: torch.dtype,
+                 device="cuda"):
+        i32 = dict(dtype=torch.int32, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.T, self.H, self.I, self.E, self.K = T, H, I, E, K
+        self.logits = torch.empty((T, E), **f32)
+        self.topk_ids = torch.empty((T, K), **i32)
+        self.topk_w = torch.empty((T, K), **f32)
+        self.offsets = torch.empty((E + 1,), **i32)
+        self.sorted_slots = torch.empty((T * K,), **i32)
+        self.slot_pos = torch.empty((T * K,), **i32)
+        self.y_sorted = torch.empty((T * K, H), **f32)
+        self.out = torch.empty((T, H), **f32)
+        xdt = MOE_F32 if act == torch.float32 else MOE_BF16
+        pb = max(16, moe_permute_workspace_bytes(T, K, E))
+        fb = max(16, moe_expert_ffn_q4_0_workspace_bytes(T, K, H, I, E, xdt))
+        self.ws_perm = torch.empty((pb,), dtype=torch.uint8, device=device)
+        self.ws_ffn = torch.empty((fb,), dtype=torch.uint8, device=device)
+
+
+def moe_layer(x, W_r, w_gate_up, w_down, K, expert_scale=None, logit_bias=None, r_scale=None,
+              bufs: Optional[LayerBuffers] = None, logits_in=None, out_act=None, residual=None,
+              stream=None) -> LayerBuffers:
+    """One routed-MoE layer: router/top-K -> permute -> expert FFN -> combine."""
+    T, H = x.shape
+    E = w_gate_up.shape[0]
+    I = w_gate_up.shape[1] // 2
+    if bufs is None:
+        bufs = LayerBuffers(T, H, I, E, K, x.dtype, device=x.device)
+    if logits_in is not None:
+        bufs.logits.copy_(logits_in)
+        moe_router_topk(None, None, bufs.logits, bufs.topk_ids, bufs.topk_w, stream=stream)
+    else:
+        moe_router_topk(x, W_r, bufs.logits, bufs.topk_ids, bufs.topk_w, r_scale=r_scale,
+                        logit_bias=logit_bias, stream=stream)
+    moe_permute(bufs.topk_ids, E, bufs.offsets, bufs.sorted_slots, bufs.slot_pos, bufs.ws_perm,
+                stream=stream)
+    moe_expert_ffn_q4_0(x, w_gate_up, w_down, K, bufs.offsets, bufs.sorted_slots, bufs.y_sorted,
+                        bufs.ws_ffn, stream=stream)
+    moe_combine(bufs.y_sorted, bufs.slot_pos, bufs.topk_ids, bufs.topk_w, expert_scale,
+                out_f32=bufs.out, out_act=out_act, residual=residual, stream=stream)
+    return bufs

@@ -1,0 +1,157 @@
+// C ABI of the routed-MoE library: argument validation, workspace layout and
+// dispatch to the gfx950 kernels.  Nothing here allocates, frees or
+// synchronises; every call only enqueues on the caller's stream.
+#include "kernels.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool dtype_ok(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+size_t act_size(int dt) { return dt == MOE_F32 ? 4 : 2; }
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+moe_status check_ekh(int64_t T, int32_t K, int32_t E) {
+    if (T < 0 || T > (int64_t)0x7FFFFFFF) return MOE_ERR_SHAPE;
+    if (E < 1 || E > MOE_MAX_E || K < 1 || K > E || K > MOE_MAX_K) return MOE_ERR_SHAPE;
+    if (T * (int64_t)K > (int64_t)0x7FFFFFFF) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+moe_status check_dim(int32_t D, int32_t maxD) {
+    return (D < 32 || D % 32 != 0 || D > maxD) ? MOE_ERR_SHAPE : MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL: return "a required pointer is NULL";
+        case MOE_ERR_SHAPE: return "a size is out of range or inconsistent";
+        case MOE_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+        case MOE_ERR_UNSUPPORTED: return "unsupported dtype or option";
+        case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOE_ERR_HIP: return "the HIP runtime reported a launch error";
+        default: return "unknown status";
+    }
+}
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+moe_status moe_router_topk(const void* x, int x_dt, int64_t T, int32_t H, const float* W_r,
+                           const float* r_scale, const float* logit_bias, int32_t E, int32_t K,
+                           float* logits, int32_t* topk_ids, float* topk_w, void* stream) {
+    moe_status s = check_ekh(T, K, E);
+    if (s != MOE_OK) return s;
+    if (W_r && (s = check_dim(H, MOE_MAX_H)) != MOE_OK) return s;
+    if (!dtype_ok(x_dt)) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_w || (W_r && !x)) return MOE_ERR_NULL;
+    if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w)) return MOE_ERR_ALIGN;
+    if (W_r && (!aligned16(x) || !aligned16(W_r) || (r_scale && !aligned16(r_scale)) ||
+                (logit_bias && !aligned16(logit_bias))))
+        return MOE_ERR_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    if (W_r) {
+        s = hip_status(moe::launch_router_logits(x, x_dt, T, H, W_r, r_scale, logit_bias, E, logits, st));
+        if (s != MOE_OK) return s;
+    }
+    return hip_status(moe::launch_topk(logits, T, E, K, topk_ids, topk_w, st));
+}
+
+size_t moe_permute_workspace_bytes(int64_t T, int32_t K, int32_t E) {
+    if (check_ekh(T, K, E) != MOE_OK) return 0;
+    return round_up(moe::permute_ws_bytes(T * K, E), 256);
+}
+
+moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E,
+                       int32_t* expert_offsets, int32_t* sorted_slots, int32_t* slot_pos, void* ws,
+                       size_t ws_bytes, void* stream) {
+    moe_status s = check_ekh(T, K, E);
+    if (s != MOE_OK) return s;
+    if (T == 0) return MOE_OK;
+    if (!topk_ids || !expert_offsets || !sorted_slots || !slot_pos) return MOE_ERR_NULL;
+    if (!aligned16(topk_ids) || !aligned16(expert_offsets) || !aligned16(sorted_slots) ||
+        !aligned16(slot_pos))
+        return MOE_ERR_ALIGN;
+    const size_t need = moe_permute_workspace_bytes(T, K, E);
+    if (need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+    if (ws && !aligned16(ws)) return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_permute(topk_ids, (int)(T * K), E, expert_offsets, sorted_slots,
+                                          slot_pos, ws, (hipStream_t)stream));
+}
+
+size_t moe_expert_ffn_q4_0_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_t I, int32_t E,
+                                           int x_dt) {
+    if (check_ekh(T, K, E) != MOE_OK || check_dim(H, MOE_MAX_H) != MOE_OK ||
+        check_dim(I, MOE_MAX_I) != MOE_OK || !dtype_ok(x_dt))
+        return 0;
+    // hidden h [T*K, I] in the activation dtype
+    return round_up((size_t)(T * K) * (size_t)I * act_size(x_dt), 256);
+}
+
+moe_status moe_expert_ffn_q4_0(const void* x, int x_dt, int64_t T, int32_t H,
+                               const void* w_gate_up, const void* w_down, int32_t I, int32_t E,
+                               int32_t K, const int32_t* expert_offsets,
+                               const int32_t* sorted_slots, float* y_sorted, void* ws,
+                               size_t ws_bytes, void* stream) {
+    moe_status s = check_ekh(T, K, E);
+    if (s != MOE_OK) return s;
+    if ((s = check_dim(H, MOE_MAX_H)) != MOE_OK || (s = check_dim(I, MOE_MAX_I)) != MOE_OK) return s;
+    if (!dtype_ok(x_dt)) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!x || !w_gate_up || !w_down || !expert_offsets || !sorted_slots || !y_sorted)
+        return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) ||
+        !aligned16(expert_offsets) || !aligned16(sorted_slots) || !aligned16(y_sorted))
+        return MOE_ERR_ALIGN;
+    const size_t need = moe_expert_ffn_q4_0_workspace_bytes(T, K, H, I, E, x_dt);
+    if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_ffn_gemv(x, x_dt, H, (const uint8_t*)w_gate_up,
+                                           (const uint8_t*)w_down, I, E, K, (int)(T * K),
+                                           expert_offsets, sorted_slots, ws, y_sorted,
+                                           (hipStream_t)stream));
+}
+
+moe_status moe_combine(const float* y_sorted, const int32_t* slot_pos, const int32_t* topk_ids,
+                       const float* topk_w, const float* expert_scale, int64_t T, int32_t K,
+                       int32_t H, const void* residual, int residual_dt, float* out_f32,
+                       void* out_act, int out_dt, void* stream) {
+    if (T < 0 || T > (int64_t)0x7FFFFFFF || K < 1 || K > MOE_MAX_K ||
+        T * (int64_t)K > (int64_t)0x7FFFFFFF)
+        return MOE_ERR_SHAPE;
+    moe_status s = check_dim(H, MOE_MAX_H);
+    if (s != MOE_OK) return s;
+    if (!dtype_ok(out_dt) || (residual && !dtype_ok(residual_dt))) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!y_sorted || !slot_pos || !topk_w || (expert_scale && !topk_ids) || (!out_f32 && !out_act))
+        return MOE_ERR_NULL;
+    if (!aligned16(y_sorted) || !aligned16(slot_pos) || !aligned16(topk_w) ||
+        (topk_ids && !aligned16(topk_ids)) || (expert_scale && !aligned16(expert_scale)) ||
+        (residual && !aligned16(residual)) || (out_f32 && !aligned16(out_f32)) ||
+        (out_act && !aligned16(out_act)))
+        return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_combine(y_sorted, slot_pos, topk_ids, topk_w, expert_scale, T, K,
+                                          H, residual, residual_dt, out_f32, out_act, out_dt,
+                                          (hipStream_t)stream));
+}
+
+moe_status moe_rmsnorm(const void* x, int x_dt, const float* w, float eps, int64_t T, int32_t H,
+                       void* out, int out_dt, void* stream) {
+    if (T < 0 || T > (int64_t)0x7FFFFFFF) return MOE_ERR_SHAPE;
+    moe_status s = check_dim(H, MOE_MAX_H);
+    if (s != MOE_OK) return s;
+    if (!dtype_ok(x_dt) || !dtype_ok(out_dt)) return MOE_ERR_UNSUPPORTED;
+    if (!(eps >= 0.f)) return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!x || !w || !out) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(out)) return MOE_ERR_ALIGN;
+    return hip_status(moe::launch_rmsnorm(x, x_dt, w, eps, T, H, out, out_dt, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,34 @@
+// Launchers of the gfx950 kernels (internal; the public ABI is sparse_moe.h).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+constexpr int ROUTER_GEMV_MAX_T = 8;   // router: per-expert GEMV up to this many tokens
+constexpr int PERM_TILE = 1024;        // permutation: slots per tile (256 threads x 4)
+constexpr int DIGIT_NMAX = 30583;      // largest |n| with 4 balanced base-16 digits: 7*(1+16+256+4096)
+
+hipError_t launch_router_logits(const void* x, int x_dt, int64_t T, int H, const float* W,
+                                const float* rsc, const float* bias, int E, float* logits,
+                                hipStream_t st);
+hipError_t launch_topk(const float* logits, int64_t T, int E, int K, int32_t* ids, float* w,
+                       hipStream_t st);
+
+size_t permute_ws_bytes(int64_t N, int E);
+hipError_t launch_permute(const int32_t* ids, int N, int E, int32_t* offsets, int32_t* sorted_slots,
+                          int32_t* slot_pos, void* ws, hipStream_t st);
+
+hipError_t launch_ffn_gemv(const void* x, int x_dt, int H, const uint8_t* w_gate_up,
+                           const uint8_t* w_down, int I, int E, int K, int N,
+                           const int32_t* offsets, const int32_t* sorted_slots, void* h_ws,
+                           float* y_sorted, hipStream_t st);
+
+hipError_t launch_combine(const float* y, const int32_t* slot_pos, const int32_t* ids,
+                          const float* w, const float* scale, int64_t T, int K, int H,
+                          const void* residual, int rdt, float* out_f32, void* out_act, int odt,
+                          hipStream_t st);
+hipError_t launch_rmsnorm(const void* x, int xdt, const float* w, float eps, int64_t T, int H,
+                          void* out, int odt, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,220 @@
+// Router logits (FP32) and top-K with renormalised softmax weights, gfx950.
+//
+// Model card "Gemma 4 26B-A4B it QAT Q4_0 with MTP assistant and vision, NInfer
+// v3 artifact", table "What is inside": the router and router scale are FP32.
+// Each token keeps the K largest logits (descending; equal logits in ascending
+// expert order) with softmax weights over the K kept logits.
+#include "kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Few tokens: one wave per expert streams its W_r row once (float4 loads) and
+// dots it with every token (T <= ROUTER_GEMV_MAX_T).
+template <int XDT>
+__global__ __launch_bounds__(256) void router_logits_gemv(const void* __restrict__ x, int T, int H,
+                                                          const float* __restrict__ W,
+                                                          const float* __restrict__ rsc,
+                                                          const float* __restrict__ bias, int E,
+                                                          float* __restrict__ logits) {
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e >= E) return;
+    const float* w = W + (int64_t)e * H;
+    float acc[ROUTER_GEMV_MAX_T];
+#pragma unroll
+    for (int t = 0; t < ROUTER_GEMV_MAX_T; ++t) acc[t] = 0.f;
+    const int H4 = H >> 2;
+    for (int j4 = lane; j4 < H4; j4 += 64) {
+        const float4 wv = reinterpret_cast<const float4*>(w)[j4];
+        float4 sv = make_float4(1.f, 1.f, 1.f, 1.f);
+        if (rsc) sv = reinterpret_cast<const float4*>(rsc)[j4];
+#pragma unroll
+        for (int t = 0; t < ROUTER_GEMV_MAX_T; ++t) {
+            if (t < T) {
+                float4 xv;
+                if (XDT == MOE_F32) {
+                    xv = reinterpret_cast<const float4*>(x)[(int64_t)t * H4 + j4];
+                } else {
+                    const uint2 b = reinterpret_cast<const uint2*>(x)[(int64_t)t * H4 + j4];
+                    xv = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
+                                     __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
+                }
+                acc[t] += (xv.x * sv.x) * wv.x;
+                acc[t] += (xv.y * sv.y) * wv.y;
+                acc[t] += (xv.z * sv.z) * wv.z;
+                acc[t] += (xv.w * sv.w) * wv.w;
+            }
+        }
+    }
+    const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+    for (int t = 0; t < ROUTER_GEMV_MAX_T; ++t) {
+        if (t < T) {
+            const float s = wave_sum(acc[t]);
+            if (lane == 0) logits[(int64_t)t * E + e] = s + b;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Many tokens: 32 tokens x 64 experts per workgroup, K-tiles of 32 staged in LDS.
+constexpr int RT_BM = 32, RT_BN = 64, RT_BK = 32;
+
+template <int XDT>
+__global__ __launch_bounds__(256) void router_logits_tiled(const void* __restrict__ x, int T, int H,
+                                                           const float* __restrict__ W,
+                                                           const float* __restrict__ rsc,
+                                                           const float* __restrict__ bias, int E,
+                                                           float* __restrict__ logits) {
+    __shared__ float As[RT_BK][RT_BM + 4];
+    __shared__ float Bs[RT_BK][RT_BN + 4];
+    const int tid = threadIdx.x;
+    const int m0 = blockIdx.x * RT_BM, n0 = blockIdx.y * RT_BN;
+    const int tx = tid & 15, ty = tid >> 4;  // experts tx*4.., tokens ty*2..
+    float acc[2][4] = {};
+    for (int k0 = 0; k0 < H; k0 += RT_BK) {
+        {   // x tile: 32 tokens x 32 k, 4 consecutive k per thread
+            const int m = tid >> 3, k4 = (tid & 7) * 4;
+            const int tok = m0 + m;
+            float v[4] = {0.f, 0.f, 0.f, 0.f};
+            if (tok < T) {
+                const int64_t off = (int64_t)tok * H + k0 + k4;
+                if (XDT == MOE_F32) {
+                    const float4 q = *reinterpret_cast<const float4*>((const float*)x + off);
+                    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+                } else {
+                    const uint2 b = *reinterpret_cast<const uint2*>((const uint16_t*)x + off);
+                    v[0] = __uint_as_float(b.x << 16); v[1] = __uint_as_float(b.x & 0xFFFF0000u);
+                    v[2] = __uint_as_float(b.y << 16); v[3] = __uint_as_float(b.y & 0xFFFF0000u);
+                }
+                if (rsc) {
+                    const float4 s = *reinterpret_cast<const float4*>(rsc + k0 + k4);
+                    v[0] *= s.x; v[1] *= s.y; v[2] *= s.z; v[3] *= s.w;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) As[k4 + i][m] = v[i];
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {  // W tile: 64 experts x 32 k
+            const int n = (tid >> 3) + 32 * r, k4 = (tid & 7) * 4;
+            float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (n0 + n < E) q = *reinterpret_cast<const float4*>(W + (int64_t)(n0 + n) * H + k0 + k4);
+            Bs[k4 + 0][n] = q.x; Bs[k4 + 1][n] = q.y; Bs[k4 + 2][n] = q.z; Bs[k4 + 3][n] = q.w;
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int k = 0; k < RT_BK; ++k) {
+            const float a0 = As[k][ty * 2], a1 = As[k][ty * 2 + 1];
+            const float4 b = *reinterpret_cast<const float4*>(&Bs[k][tx * 4]);
+            acc[0][0] += a0 * b.x; acc[0][1] += a0 * b.y; acc[0][2] += a0 * b.z; acc[0][3] += a0 * b.w;
+            acc[1][0] += a1 * b.x; acc[1][1] += a1 * b.y; acc[1][2] += a1 * b.z; acc[1][3] += a1 * b.w;
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int tok = m0 + ty * 2 + i;
+        if (tok >= T) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = n0 + tx * 4 + j;
+            if (e < E) logits[(int64_t)tok * E + e] = acc[i][j] + (bias ? bias[e] : 0.f);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Top-K: one wave per token; each lane holds experts lane, lane+64, ...
+__global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ logits, int64_t T,
+                                                    int E, int K, int32_t* __restrict__ ids,
+                                                    float* __restrict__ w) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const float* l = logits + t * E;
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? l[e] : 0.f;
+    }
+    uint32_t taken = 0;
+    float selv[MOE_MAX_K];
+    int seli[MOE_MAX_K];
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_K; ++k) {
+        selv[k] = 0.f;
+        seli[k] = 0;
+        if (k < K) {
+            float bv = -INFINITY;
+            int bi = 0x7FFFFFFF;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = lane + 64 * i;
+                if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
+                    bv = v[i];
+                    bi = e;
+                }
+            }
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) {
+                const float ov = __shfl_xor(bv, m, 64);
+                const int oi = __shfl_xor(bi, m, 64);
+                if (ov > bv || (ov == bv && oi < bi)) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+            selv[k] = bv;
+            seli[k] = bi;
+            if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_K; ++k)
+        if (k < K) s += expf(selv[k] - selv[0]);
+    float myv = 0.f;
+    int myi = 0;
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_K; ++k)
+        if (k == lane) {
+            myv = selv[k];
+            myi = seli[k];
+        }
+    if (lane < K) {
+        ids[t * K + lane] = myi;
+        w[t * K + lane] = expf(myv - selv[0]) / s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_router_logits(const void* x, int x_dt, int64_t T, int H, const float* W,
+                                const float* rsc, const float* bias, int E, float* logits,
+                                hipStream_t st) {
+    if (T <= ROUTER_GEMV_MAX_T) {
+        dim3 grid((E + 3) / 4);
+        if (x_dt == MOE_F32)
+            router_logits_gemv<MOE_F32><<<grid, 256, 0, st>>>(x, (int)T, H, W, rsc, bias, E, logits);
+        else
+            router_logits_gemv<MOE_BF16><<<grid, 256, 0, st>>>(x, (int)T, H, W, rsc, bias, E, logits);
+    } else {
+        dim3 grid((unsigned)((T + RT_BM - 1) / RT_BM), (E + RT_BN - 1) / RT_BN);
+        if (x_dt == MOE_F32)
+            router_logits_tiled<MOE_F32><<<grid, 256, 0, st>>>(x, (int)T, H, W, rsc, bias, E, logits);
+        else
+            router_logits_tiled<MOE_BF16><<<grid, 256, 0, st>>>(x, (int)T, H, W, rsc, bias, E, logits);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* logits, int64_t T, int E, int K, int32_t* ids, float* w,
+                       hipStream_t st) {
+    dim3 grid((unsigned)((T + 3) / 4));
+    topk_softmax<<<grid, 256, 0, st>>>(logits, T, E, K, ids, w);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,108 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports
+every function include/sparse_moe.h declares, and rejects bad arguments with
+the documented status before enqueueing anything.
+
+Every call below fails validation, so no kernel is launched and the fake
+device addresses are never touched."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_moe.h")
+
+binding = pytest.importorskip("sparse_moe_amd.binding")
+lib = binding.lib
+
+OK, NULL, SHAPE, ALIGN, UNSUP, WS = 0, 1, 2, 3, 4, 5
+A = C.c_void_p(0x100000)        # 16-byte aligned fake device address (never dereferenced)
+B = C.c_void_p(0x200000)
+MIS = C.c_void_p(0x100004)      # misaligned
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(binding.SIGNATURES)
+    assert lib.moe_abi_version() == 1
+
+
+def test_status_strings():
+    for s in range(7):
+        assert lib.moe_status_string(s)
+    assert lib.moe_status_string(99) == b"unknown status"
+
+
+def test_router_validation():
+    f = lib.moe_router_topk
+    # (x, x_dt, T, H, W_r, r_scale, bias, E, K, logits, ids, w, stream)
+    assert f(A, 0, 4, 256, A, None, None, 0, 1, A, A, A, None) == SHAPE        # E = 0
+    assert f(A, 0, 4, 256, A, None, None, 8, 9, A, A, A, None) == SHAPE        # K > E
+    assert f(A, 0, 4, 256, A, None, None, 300, 2, A, A, A, None) == SHAPE      # E > 256
+    assert f(A, 0, 4, 256, A, None, None, 64, 17, A, A, A, None) == SHAPE      # K > 16
+    assert f(A, 0, 4, 100, A, None, None, 8, 2, A, A, A, None) == SHAPE        # H % 32
+    assert f(A, 0, -1, 256, A, None, None, 8, 2, A, A, A, None) == SHAPE       # T < 0
+    assert f(A, 5, 4, 256, A, None, None, 8, 2, A, A, A, None) == UNSUP        # dtype
+    assert f(None, 0, 0, 256, None, None, None, 8, 2, None, None, None, None) == OK  # T = 0
+    assert f(None, 0, 4, 256, A, None, None, 8, 2, A, A, A, None) == NULL      # x
+    assert f(A, 0, 4, 256, A, None, None, 8, 2, None, A, A, None) == NULL      # logits
+    assert f(A, 0, 4, 256, A, None, None, 8, 2, A, A, MIS, None) == ALIGN
+    assert f(MIS, 0, 4, 256, A, None, None, 8, 2, A, A, A, None) == ALIGN
+    assert f(A, 0, 4, 256, A, MIS, None, 8, 2, A, A, A, None) == ALIGN
+
+
+def test_permute_validation_and_workspace():
+    f = lib.moe_permute
+    assert lib.moe_permute_workspace_bytes(4, 2, 8) == 0           # one tile: no workspace
+    big = lib.moe_permute_workspace_bytes(4096, 8, 128)
+    assert big >= (2 * 32 * 128 + 32768) * 4 and big % 256 == 0
+    assert f(A, 4096, 8, 128, A, A, A, None, 0, None) == WS
+    assert f(A, 4096, 8, 128, A, A, A, A, 16, None) == WS
+    assert f(A, 4, 2, 8, None, A, A, None, 0, None) == NULL
+    assert f(A, 4, 2, 8, A, MIS, A, None, 0, None) == ALIGN
+    assert f(A, 4, 9, 8, A, A, A, None, 0, None) == SHAPE
+    assert f(None, 0, 2, 8, None, None, None, None, 0, None) == OK
+    assert f(A, 2 ** 30, 8, 128, A, A, A, A, 1 << 40, None) == SHAPE   # T*K >= 2^31
+
+
+def test_ffn_validation_and_workspace():
+    f = lib.moe_expert_ffn_q4_0
+    ws = lib.moe_expert_ffn_q4_0_workspace_bytes(4096, 8, 2816, 704, 128, 1)
+    assert ws >= 4096 * 8 * 704 * 2
+    assert lib.moe_expert_ffn_q4_0_workspace_bytes(4, 2, 250, 64, 8, 0) == 0   # bad H
+    # (x, x_dt, T, H, w_gu, w_dn, I, E, K, offsets, sorted, y, ws, ws_bytes, stream)
+    assert f(A, 1, 4096, 2816, A, A, 704, 128, 8, A, A, A, A, 16, None) == WS
+    assert f(A, 1, 4096, 2816, A, A, 704, 128, 8, A, A, A, None, ws, None) == WS
+    assert f(A, 1, 4, 2816, A, A, 700, 128, 8, A, A, A, A, ws, None) == SHAPE   # I % 32
+    assert f(A, 1, 4, 8192, A, A, 704, 128, 8, A, A, A, A, ws, None) == SHAPE   # H > max
+    assert f(A, 1, 4, 2816, None, A, 704, 128, 8, A, A, A, A, ws, None) == NULL
+    assert f(A, 1, 4, 2816, MIS, A, 704, 128, 8, A, A, A, A, ws, None) == ALIGN
+    assert f(A, 3, 4, 2816, A, A, 704, 128, 8, A, A, A, A, ws, None) == UNSUP
+    assert f(None, 1, 0, 2816, None, None, 704, 128, 8, None, None, None, None, 0, None) == OK
+
+
+def test_combine_and_rmsnorm_validation():
+    f = lib.moe_combine
+    # (y, slot_pos, ids, w, scale, T, K, H, residual, rdt, out_f32, out_act, odt, stream)
+    assert f(A, A, A, A, A, 4, 2, 256, None, 0, None, None, 0, None) == NULL   # no output
+    assert f(A, A, None, A, A, 4, 2, 256, None, 0, A, None, 0, None) == NULL   # scale needs ids
+    assert f(A, A, A, A, A, 4, 2, 250, None, 0, A, None, 0, None) == SHAPE
+    assert f(A, A, A, A, A, 4, 2, 256, None, 0, A, A, 9, None) == UNSUP
+    assert f(A, A, A, A, A, 4, 2, 256, MIS, 0, A, None, 0, None) == ALIGN
+    assert f(None, None, None, None, None, 0, 2, 256, None, 0, None, None, 0, None) == OK
+    g = lib.moe_rmsnorm
+    assert g(A, 1, A, C.c_float(1e-6), 4, 100, A, 1, None) == SHAPE
+    assert g(A, 1, None, C.c_float(1e-6), 4, 256, A, 1, None) == NULL
+    assert g(A, 1, A, C.c_float(-1.0), 4, 256, A, 1, None) == SHAPE
+    assert g(A, 1, A, C.c_float(1e-6), 4, 256, MIS, 1, None) == ALIGN
+    assert g(None, 1, None, C.c_float(1e-6), 0, 256, None, 1, None) == OK

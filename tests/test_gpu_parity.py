@@ -1,0 +1,106 @@
+"""GPU parity of the four C-ABI calls against the CPU oracle, on the seeded
+workloads at their full sizes and on edge cases (shape sweep, T = 0,
+determinism, unwritten-output sentinels)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+from sparse_moe_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _run(L, logits_in=None, token_sample=None):
+    print("case: %s T=%d H=%d E=%d K=%d I=%d act=%s" % (L.spec.name, L.x.shape[0], L.spec.H,
+                                                        L.spec.E, L.spec.K, L.spec.I, L.spec.act),
+          flush=True)
+    g, bufs = parity.run_gpu_layer(L, logits_in)
+    res = parity.check_layer(L, g, logits_in=logits_in, token_sample=token_sample)
+    print("  ->", res, flush=True)
+    return g, res
+
+
+def test_tiny_layer():
+    _run(synth.make_layer(synth.SPECS[0]))
+
+
+def test_decode_1_token():
+    _run(synth.make_layer(synth.SPECS[1]))
+
+
+def test_decode_8_tokens():
+    g, res = _run(synth.make_layer(synth.SPECS[2]))
+    assert 30 <= res["distinct_experts"] <= 64
+
+
+def test_decode_8_tokens_injected_uniform_logits():
+    spec = synth.SPECS[2]
+    L = synth.make_layer(spec)
+    lg = synth.uniform_logits(spec.T, spec.E, spec.seed)
+    _run(L, logits_in=lg)
+
+
+def test_prefill_4096_tokens_sampled():
+    spec = synth.SPECS[3]
+    L = synth.make_layer(spec)
+    sample = np.random.default_rng(3).choice(spec.T, size=12, replace=False)
+    sample = np.concatenate([[0, spec.T - 1], sample])
+    _run(L, token_sample=sample)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 7, 8, 33, 512])
+@pytest.mark.parametrize("E,K", [(8, 1), (8, 2), (128, 8), (128, 1)])
+def test_shape_sweep(T, E, K):
+    base = synth.SPECS[0] if E == 8 else synth.SPECS[2]
+    spec = synth.LayerSpec(**{**base.__dict__, "E": E, "K": K, "T": T,
+                              "name": "sweep-T%d-E%d-K%d" % (T, E, K)})
+    L = synth.make_layer(spec, seed=100 + T)
+    sample = None if (E == 8 or T <= 8) else np.arange(0, T, max(1, T // 6))
+    _run(L, token_sample=sample)
+
+
+def test_odd_block_count_rows():
+    # H = 32 * 9 and I = 32 * 3: rows with an odd number of Q4_0 blocks
+    spec = synth.LayerSpec("odd-blocks", H=288, E=8, K=2, I=96, T=5, act="f32",
+                           router_std=1 / 17, seed=7)
+    _run(synth.make_layer(spec))
+
+
+def test_zero_tokens_is_a_noop():
+    from sparse_moe_amd import binding
+    L = synth.make_layer(synth.SPECS[0], T=1)
+    x = parity.to_dev(L.x)[:0]
+    bufs = binding.LayerBuffers(0, 256, 64, 8, 2, torch.float32)
+    binding.moe_layer(x, parity.to_dev(L.w_router), parity.to_dev(L.w_gate_up),
+                      parity.to_dev(L.w_down), 2, bufs=bufs)
+    torch.cuda.synchronize()
+
+
+def test_deterministic_and_fully_written():
+    from sparse_moe_amd import binding
+    spec = synth.SPECS[2]
+    L = synth.make_layer(spec)
+    outs = []
+    for rep in range(2):
+        bufs = binding.LayerBuffers(spec.T, spec.H, spec.I, spec.E, spec.K, torch.bfloat16)
+        for t in (bufs.logits, bufs.topk_w, bufs.y_sorted, bufs.out):
+            t.fill_(float("nan"))
+        for t in (bufs.topk_ids, bufs.offsets, bufs.sorted_slots, bufs.slot_pos):
+            t.fill_(-1)
+        g, _ = parity.run_gpu_layer(L, bufs=bufs)
+        for k, v in g.items():
+            if v.dtype.kind == "f":
+                assert np.all(np.isfinite(v)), k
+            else:
+                assert np.all(v >= 0), k
+        outs.append(g)
+    for k in outs[0]:
+        assert np.array_equal(outs[0][k].view(np.uint8), outs[1][k].view(np.uint8)), k
