@@ -112,7 +112,7 @@ moe_status moe_expert_ffn_q4_0(const void* x, int x_dt, int64_t T, int32_t H,
     const size_t need = moe_expert_ffn_q4_0_workspace_bytes(T, K, H, I, E, x_dt);
     if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
     if (!aligned16(ws)) return MOE_ERR_ALIGN;
-    return hip_status(moe::launch_ffn_gemv(x, x_dt, H, (const uint8_t*)w_gate_up,
+    return hip_status(moe::launch_ffn_gemv(x, x_dt, T, H, (const uint8_t*)w_gate_up,
                                            (const uint8_t*)w_down, I, E, K, (int)(T * K),
                                            expert_offsets, sorted_slots, ws, y_sorted,
                                            (hipStream_t)stream));

@@ -39,25 +39,58 @@ MOE_DEV float f16_bits_to_f32(uint32_t h) {
 }
 
 // ---- GELU with the tanh approximation ----------------------------------------
+// 0.5 z (1 + tanh(a)) = z / (1 + exp(-2a)), a = sqrt(2/pi) (z + 0.044715 z^3);
+// exp through the hardware exp2.
 MOE_DEV float gelu_tanh(float z) {
-    const float c = 0.7978845608028654f;  // sqrt(2/pi)
-    return 0.5f * z * (1.0f + tanhf(c * (z + 0.044715f * z * z * z)));
+    const float c2 = 2.0f * 0.7978845608028654f * 1.4426950408889634f;  // 2 sqrt(2/pi) log2(e)
+    const float a = c2 * fmaf(0.044715f * z, z * z, z);
+    return z / (1.0f + exp2f(-a));
 }
 
-// ---- wave64 reductions --------------------------------------------------------
-MOE_DEV float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
+// ---- wave64 reductions through DPP (no LDS round trips) --------------------------
+// update_dpp(old, src, ctrl, row_mask, bank_mask, bound_ctrl): lanes whose row is
+// masked off keep `old`.
+template <int CTRL, int ROW_MASK = 0xF>
+MOE_DEV float dpp_f32(float old, float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL,
+                                                      ROW_MASK, 0xF, false));
 }
 
-// sum over aligned groups of G lanes (G a power of two <= 64); every lane of a
-// group receives the group's sum
+constexpr int DPP_QUAD_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_BCAST15 = 0x142;
+constexpr int DPP_ROW_BCAST31 = 0x143;
+
+// Sum over aligned groups of G lanes (G a power of two <= 64).  The result is
+// valid in lane G-1 of each group (and in every lane of the group for G <= 16).
+// Every lane of the wave must be active.
 template <int G>
 MOE_DEV float group_sum(float v) {
-#pragma unroll
-    for (int m = G / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    if (G >= 2) v += dpp_f32<DPP_QUAD_XOR1>(v, v);
+    if (G >= 4) v += dpp_f32<DPP_QUAD_XOR2>(v, v);
+    if (G >= 8) v += dpp_f32<DPP_ROW_HALF_MIRROR>(v, v);
+    if (G >= 16) v += dpp_f32<DPP_ROW_MIRROR>(v, v);
+    if (G >= 32) v += dpp_f32<DPP_ROW_BCAST15, 0xA>(0.f, v);
+    if (G >= 64) v += dpp_f32<DPP_ROW_BCAST31, 0xC>(0.f, v);
     return v;
+}
+
+// Maximum over the whole wave, returned uniformly (read from lane 63).
+MOE_DEV float wave_max(float v) {
+    v = fmaxf(v, dpp_f32<DPP_QUAD_XOR1>(v, v));
+    v = fmaxf(v, dpp_f32<DPP_QUAD_XOR2>(v, v));
+    v = fmaxf(v, dpp_f32<DPP_ROW_HALF_MIRROR>(v, v));
+    v = fmaxf(v, dpp_f32<DPP_ROW_MIRROR>(v, v));
+    v = fmaxf(v, dpp_f32<DPP_ROW_BCAST15, 0xA>(-INFINITY, v));
+    v = fmaxf(v, dpp_f32<DPP_ROW_BCAST31, 0xC>(-INFINITY, v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+MOE_DEV float wave_sum(float v) {
+    v = group_sum<64>(v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 MOE_DEV int lane_id() { return __lane_id(); }

@@ -28,57 +28,56 @@ namespace moe {
 // ---- activation digits -------------------------------------------------------
 // Word (m, k) (m = qs dword 0..3, k = digit 0..3) holds digit k of the 8
 // elements that the 8 nibbles of qs dword m encode: nibble p <-> element
-// 4m + (p >> 1) + 16 (p & 1).
+// 4m + (p >> 1) + 16 (p & 1).  In LDS, word i (= 4m + k) of block b of token
+// slot t sits at dig[(t * 16 + i) * nbp + b] (nbp = blocks rounded up to even),
+// so lanes reading the 2 blocks of their pair read consecutive 8-byte words.
+// A quad of lanes digitises one 32-element block:
+// lane m of the quad owns elements 4m..4m+3 and 4m+16..4m+19, so it produces
+// the 4 words of qs dword m; the block maximum comes from a quad reduction.
+// Every lane of a quad must be active.
 template <int ADT>
-MOE_DEV void quantize_block32(const void* src, int64_t e0, uint32_t* words, float* scale) {
-    float v[32];
+MOE_DEV void load_quarter(const void* src, int64_t e0, int m, float v[8]) {
     if (ADT == MOE_F32) {
-        const float4* p = reinterpret_cast<const float4*>((const float*)src + e0);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float4 q = p[i];
-            v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
-        }
+        const float4 lo = reinterpret_cast<const float4*>((const float*)src + e0 + 4 * m)[0];
+        const float4 hi = reinterpret_cast<const float4*>((const float*)src + e0 + 16 + 4 * m)[0];
+        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+        v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
     } else {
-        const uint4* p = reinterpret_cast<const uint4*>((const uint16_t*)src + e0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint4 q = p[i];
-            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
-                v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-            }
-        }
+        const uint2 lo = reinterpret_cast<const uint2*>((const uint16_t*)src + e0 + 4 * m)[0];
+        const uint2 hi = reinterpret_cast<const uint2*>((const uint16_t*)src + e0 + 16 + 4 * m)[0];
+        v[0] = __uint_as_float(lo.x << 16); v[1] = __uint_as_float(lo.x & 0xFFFF0000u);
+        v[2] = __uint_as_float(lo.y << 16); v[3] = __uint_as_float(lo.y & 0xFFFF0000u);
+        v[4] = __uint_as_float(hi.x << 16); v[5] = __uint_as_float(hi.x & 0xFFFF0000u);
+        v[6] = __uint_as_float(hi.y << 16); v[7] = __uint_as_float(hi.y & 0xFFFF0000u);
     }
+}
+
+MOE_DEV void digitize_quarter(const float v[8], int m, uint32_t* words, int wstride, float* scale) {
     float amax = 0.f;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    uint32_t wd[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) wd[i] = 0;
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    amax = fmaxf(amax, dpp_f32<DPP_QUAD_XOR1>(amax, amax));
+    amax = fmaxf(amax, dpp_f32<DPP_QUAD_XOR2>(amax, amax));
+    uint32_t wd[4] = {0u, 0u, 0u, 0u};
     float s = 0.f;
     if (amax > 0.f) {
         const float inv = (float)DIGIT_NMAX / amax;
         s = amax / (float)DIGIT_NMAX;
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
+        for (int j = 0; j < 8; ++j) {
             int n = (int)rintf(v[j] * inv);
             n = max(-DIGIT_NMAX, min(DIGIT_NMAX, n));
-            const int m = (j & 15) >> 2;
-            const int p = ((j & 3) << 1) | (j >> 4);
+            // n + 0x8888 = sum_k h_k 16^k with hex digits h_k, so n = sum_k (h_k - 8) 16^k:
+            // the balanced digits are h_k - 8, whose 4-bit two's complement is h_k ^ 8.
+            const uint32_t u = (uint32_t)(n + 0x8888) ^ 0x8888u;
+            const int p = ((j & 3) << 1) | (j >> 2);   // nibble of element 4m+(j&3)+16(j>>2)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int d = ((n + 8) & 15) - 8;
-                wd[m * 4 + k] |= (uint32_t)(d & 15) << (4 * p);
-                n = (n - d) >> 4;
-            }
+            for (int k = 0; k < 4; ++k) wd[k] |= ((u >> (4 * k)) & 15u) << (4 * p);
         }
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) words[i] = wd[i];
-    *scale = s;
+    for (int k = 0; k < 4; ++k) words[(4 * m + k) * wstride] = wd[k];
+    if (m == 0) *scale = s;
 }
 
 // signed 4-bit codes (q - 8) of one Q4_0 block times the 4 digit words of each
@@ -97,74 +96,113 @@ MOE_DEV int block_idot(const uint32_t q[4], const uint32_t* x16) {
 }
 
 // Scales and qs dwords of a block pair: block A at bytes 0..17, block B at
-// bytes 18..35 of the lane's 36-byte window (always 4-byte aligned).  nh = how
-// many of the two blocks exist (the last pair of a row with an odd block count
-// has one: only its 18 bytes are read).  Missing blocks get a zero scale.
+// bytes 18..35 of a lane's 36-byte window.  nh = how many of the two blocks
+// exist (the last pair of a row with an odd block count has one); a missing
+// block gets a zero scale, so its products vanish.
 struct PairDec {
     float dA, dB;
     uint32_t qA[4], qB[4];
 };
 
-MOE_DEV PairDec load_pair(const uint8_t* p, int nh) {
-    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-    u32x4a4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    uint32_t w8 = 0u, tail = 0u;
-    if (nh >= 1) a = __builtin_nontemporal_load(reinterpret_cast<const u32x4a4*>(q));
-    if (nh == 2) {
-        b = __builtin_nontemporal_load(reinterpret_cast<const u32x4a4*>(q + 4));
-        w8 = __builtin_nontemporal_load(q + 8);
-    } else if (nh == 1) {
-        tail = *reinterpret_cast<const uint16_t*>(p + 16);
+// window read from LDS.  EVEN_NB: rows hold an even number of blocks, so every
+// window starts 4-byte aligned; otherwise read it as 2-byte halves.
+template <bool EVEN_NB>
+MOE_DEV PairDec lds_pair(const uint8_t* p, int nh) {
+    uint32_t w[9];
+    if (EVEN_NB) {
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+#pragma unroll
+        for (int i = 0; i < 9; ++i) w[i] = q[i];
+    } else {
+        const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
+#pragma unroll
+        for (int i = 0; i < 9; ++i) w[i] = (uint32_t)q[2 * i] | ((uint32_t)q[2 * i + 1] << 16);
     }
-    const uint32_t w4 = (nh == 2) ? b.x : tail;
-    PairDec r;
-    r.dA = f16_bits_to_f32(a.x);
-    r.dB = f16_bits_to_f32(w4 >> 16);
-    r.qA[0] = __builtin_amdgcn_perm(a.y, a.x, 0x05040302u);
-    r.qA[1] = __builtin_amdgcn_perm(a.z, a.y, 0x05040302u);
-    r.qA[2] = __builtin_amdgcn_perm(a.w, a.z, 0x05040302u);
-    r.qA[3] = __builtin_amdgcn_perm(w4, a.w, 0x05040302u);
-    r.qB[0] = b.y;
-    r.qB[1] = b.z;
-    r.qB[2] = b.w;
-    r.qB[3] = w8;
-    return r;
+    PairDec d;
+    d.dA = nh >= 1 ? f16_bits_to_f32(w[0]) : 0.f;
+    d.dB = nh == 2 ? f16_bits_to_f32(w[4] >> 16) : 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        d.qA[m] = __builtin_amdgcn_perm(w[m + 1], w[m], 0x05040302u);
+        d.qB[m] = w[5 + m];
+    }
+    return d;
+}
+
+// Load bytes [s0, s1) of a weight matrix with coalesced 16-byte loads
+// (consecutive lanes read consecutive 16 bytes) into registers; store_span then
+// writes them to the wave's LDS region.  The copy starts at the 16-byte boundary
+// at or below s0; the matrix base is 16-byte aligned and its size a multiple of
+// 16, so no chunk leaves the matrix.  Exactly NCH loads are issued (lanes past
+// the span re-read its last chunk), so the number of loads in flight is known at
+// compile time and the activations, loaded earlier, can be used while these are
+// still in flight.  Returns the LDS offset of byte s0.
+template <int NCH>
+MOE_DEV int load_span(const uint8_t* mat, int64_t s0, int64_t s1, int lane, u32x4a4 (&v)[NCH]) {
+    const int64_t a0 = s0 & ~(int64_t)15;
+    const int last = (int)((s1 - a0 + 15) >> 4) - 1;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int c = min(64 * i + lane, last);
+        v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4a4*>(mat + a0 + 16 * (int64_t)c));
+    }
+    return (int)(s0 - a0);
+}
+
+template <int NCH>
+MOE_DEV void store_span(uint8_t* lds_wave, int lane, const u32x4a4 (&v)[NCH]) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+        *reinterpret_cast<uint4*>(lds_wave + 1024 * i + 16 * lane) = make_uint4(v[i].x, v[i].y, v[i].z, v[i].w);
 }
 
 // ---- kernel --------------------------------------------------------------------
 // MODE 0: gate/up rows of the [gate; up] parent -> h = GELU_tanh(g) * u (act dtype)
 // MODE 1: down rows -> y (fp32)
-// One workgroup = 4 waves; each wave owns UPW units; a unit is RPS = 64/LPR
-// output rows (MODE 0: RPS gate rows and the RPS matching up rows).
-// The weights of the wave's units are loaded once into registers; tokens of
-// the expert are then processed in chunks of TC.
-template <int MODE, int ADT, int LPR, int TC, int UPW>
+// One workgroup = 4 waves.  A wave owns UPW steps of RPS = 64/LPR output rows
+// (MODE 0: the gate rows and the matching up rows); it stages those rows in its
+// own LDS region with coalesced loads, then lane (g, q) of a step computes block
+// pair q of row g from LDS.  Tokens of the expert are processed in chunks of TC
+// whose activation digits are staged in LDS once per workgroup.
+template <int MODE, int ADT, int LPR, int TC, int UPW, bool EVEN_NB>
 __global__ __launch_bounds__(256) void ffn_gemv_q4_0(
     const uint8_t* __restrict__ W, int nb, int I, int H, const void* __restrict__ act,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slots, int K, int E,
-    void* __restrict__ out) {
+    void* __restrict__ out, int wave_lds_bytes) {
     constexpr int RPS = 64 / LPR;
-    constexpr int NR = (MODE == 0) ? 2 : 1;  // rows per unit and lane (gate + up)
-    extern __shared__ uint32_t lds[];        // [TC][nb][16] digit words, then [TC][nb] scales
-    __shared__ int s_e, s_wcnt[4];
+    constexpr int RPW = RPS * UPW;           // rows (MODE 0: row pairs) per wave
+    constexpr int NR = (MODE == 0) ? 2 : 1;  // spans per wave (gate, up)
+    // staging loads per span: rows hold at most 2*LPR blocks (36*LPR bytes)
+    constexpr int NCH = (RPW * 36 * LPR + 15 + 1023) / 1024;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ int s_e, s_p0, s_n, s_wcnt[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     // -- which expert: the blockIdx.y-th expert with at least one slot
     {
         const int e = tid;
-        const bool ne = e < E && offsets[e + 1] > offsets[e];
+        int o0 = 0, o1 = 0;
+        if (e < E) {
+            o0 = offsets[e];
+            o1 = offsets[e + 1];
+        }
+        const bool ne = o1 > o0;
         const uint64_t b = __ballot(ne);
         if (tid == 0) s_e = -1;
         if (lane == 0) s_wcnt[wave] = __popcll(b);
         __syncthreads();
         int before = __popcll(b & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
         for (int w = 0; w < wave; ++w) before += s_wcnt[w];
-        if (ne && before == (int)blockIdx.y) s_e = e;
+        if (ne && before == (int)blockIdx.y) {
+            s_e = e;
+            s_p0 = o0;
+            s_n = o1 - o0;
+        }
         __syncthreads();
     }
     const int e = s_e;
     if (e < 0) return;
-    const int p0 = offsets[e], ne_tok = offsets[e + 1] - p0;
+    const int p0 = s_p0, ne_tok = s_n;
 
     const int rows_out = (MODE == 0) ? I : H;            // outputs per expert
     const int rows_tot = (MODE == 0) ? 2 * I : H;        // stored rows per expert
@@ -172,144 +210,243 @@ __global__ __launch_bounds__(256) void ffn_gemv_q4_0(
     const uint8_t* We = W + (int64_t)e * rows_tot * row_bytes;
     const int g = lane / LPR, q = lane % LPR;
     const int nblk_here = min(2, max(0, nb - 2 * q));
-    const int unit0 = (blockIdx.x * 4 + wave) * UPW;
+    const int row0 = (blockIdx.x * 4 + wave) * RPW;      // first output row of this wave
+    const int nrows = max(0, min(RPW, rows_out - row0));
 
-    // -- weights of this wave's units: loaded once
-    PairDec wt[UPW][NR];
-#pragma unroll
-    for (int u = 0; u < UPW; ++u) {
-        const int row = (unit0 + u) * RPS + g;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const int srow = row + r * I;
-            const int nh = row < rows_out ? nblk_here : 0;
-            wt[u][r] = load_pair(We + srow * row_bytes + 36 * q, nh);
-        }
-    }
-
-    uint32_t* dig = lds;
-    float* dsc = reinterpret_cast<float*>(lds + TC * nb * 16);
+    uint8_t* wl = smem + wave * wave_lds_bytes;
+    const int span_bytes = NCH * 1024 - 16;
+    const int nbp = (nb + 1) & ~1;  // blocks per activation row, rounded up to a pair
+    uint32_t* dig = reinterpret_cast<uint32_t*>(smem + 4 * wave_lds_bytes);
+    float* dsc = reinterpret_cast<float*>(dig + TC * 16 * nbp);
     const int in_len = (MODE == 0) ? H : I;
-    for (int c0 = 0; c0 < ne_tok; c0 += TC) {
-        // -- digits of the chunk's activation rows into LDS
-        __syncthreads();
-        for (int task = tid; task < TC * nb; task += 256) {
-            const int t = task / nb, b = task % nb;
-            const int p = p0 + c0 + t;
-            if (c0 + t < ne_tok) {
-                const int64_t src_row = (MODE == 0) ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
-                quantize_block32<ADT>(act, src_row * in_len + b * 32, dig + (t * nb + b) * 16,
-                                      dsc + t * nb + b);
-            } else {
+    constexpr int NTASK = 2 * TC;  // quarter-block tasks per thread: TC * 128 blocks * 4 / 256
+
+    // activation rows of a chunk -> registers (one quarter block per task)
+    float xv[NTASK][8];
+    auto load_x = [&](int c0) {
+        int64_t src_row[TC];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) dig[(t * nb + b) * 16 + i] = 0;
-                dsc[t * nb + b] = 0.f;
-            }
+        for (int t = 0; t < TC; ++t) {
+            const int p = __builtin_amdgcn_readfirstlane(p0 + min(c0 + t, ne_tok - 1));
+            src_row[t] = (MODE == 0) ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
         }
-        __syncthreads();
-        float acc[UPW][NR][TC];
 #pragma unroll
-        for (int u = 0; u < UPW; ++u)
+        for (int i = 0; i < NTASK; ++i) {
+            const int task = tid + 256 * i;
+            const int m = task & 3, tb = task >> 2;
+            const int t = tb / nb, b = tb % nb;
+            int64_t row = src_row[0];
 #pragma unroll
-            for (int r = 0; r < NR; ++r)
+            for (int j = 1; j < TC; ++j)
+                if (t == j) row = src_row[j];
+            // unconditional (clamped) so that the count of loads in flight is static
+            const bool ok = task < TC * nb * 4 && c0 + t < ne_tok;
+            load_quarter<ADT>(act, ok ? row * in_len + b * 32 : 0, m, xv[i]);
+        }
+    };
+    // registers -> activation digits in LDS
+    auto digitize = [&](int c0) {
 #pragma unroll
-                for (int t = 0; t < TC; ++t) acc[u][r][t] = 0.f;
-        if (nblk_here > 0) {
-#pragma unroll
-            for (int t = 0; t < TC; ++t) {
-                uint32_t xa[16], xb[16];
-                const uint32_t* da = dig + (t * nb + 2 * q) * 16;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) xa[i] = da[i];
-                const float sa = dsc[t * nb + 2 * q];
-                float sb = 0.f;
-                if (nblk_here == 2) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) xb[i] = da[16 + i];
-                    sb = dsc[t * nb + 2 * q + 1];
+        for (int i = 0; i < NTASK; ++i) {
+            const int task = tid + 256 * i;
+            if (task < TC * nb * 4) {
+                const int m = task & 3, tb = task >> 2;
+                const int t = tb / nb, b = tb % nb;
+                uint32_t* wbase = dig + (int64_t)t * 16 * nbp + b;
+                if (c0 + t < ne_tok) {
+                    digitize_quarter(xv[i], m, wbase, nbp, dsc + t * nbp + b);
                 } else {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) xb[i] = 0;
+                    for (int k = 0; k < 4; ++k) wbase[(4 * m + k) * nbp] = 0u;
+                    if (m == 0) dsc[t * nbp + b] = 0.f;
                 }
-#pragma unroll
-                for (int u = 0; u < UPW; ++u)
-#pragma unroll
-                    for (int r = 0; r < NR; ++r) {
-                        const int ia = block_idot(wt[u][r].qA, xa);
-                        const int ib = block_idot(wt[u][r].qB, xb);
-                        acc[u][r][t] = fmaf(wt[u][r].dA * sa, (float)ia, acc[u][r][t]);
-                        acc[u][r][t] = fmaf(wt[u][r].dB * sb, (float)ib, acc[u][r][t]);
-                    }
             }
         }
-        // -- reduce over the LPR lanes of a row, write
+    };
+
+    load_x(0);  // first: so that waiting for the activations does not wait for the weights
+
+    // -- this wave's rows: all loads in flight at once (into registers)
+    int loff[NR];
+    u32x4a4 wreg[NR][NCH];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {  // unconditional: waves past the last row load one chunk
+        const int64_t s0 = nrows > 0 ? (int64_t)(row0 + r * I) * row_bytes : 0;
+        const int64_t s1 = nrows > 0 ? s0 + nrows * row_bytes : 16;
+        loff[r] = load_span<NCH>(We, s0, s1, lane, wreg[r]);
+    }
+    if (nbp != nb) {  // the pad block of an odd block count reads as zero
+        for (int i = tid; i < TC * 16; i += 256) dig[i * nbp + nb] = 0u;
+        for (int i = tid; i < TC; i += 256) dsc[i * nbp + nb] = 0.f;
+    }
+
+    // products of the staged rows with the chunk's digits, reductions, outputs
+    auto compute = [&](int c0) {
+        if (c0 == 0) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) store_span<NCH>(wl + r * (span_bytes + 16), lane, wreg[r]);
+        }
+        __syncthreads();  // digits of every wave and this wave's rows are in LDS
+        const int qp = min(q, nbp / 2 - 1);   // lanes past the row's pairs read a valid pair
+        uint32_t xa[TC][16], xb[TC][16];
+        float sa[TC], sb[TC];
+#pragma unroll
+        for (int t = 0; t < TC; ++t) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const uint2 v = reinterpret_cast<const uint2*>(dig + (t * 16 + i) * nbp)[qp];
+                xa[t][i] = v.x;
+                xb[t][i] = v.y;
+            }
+            const float2 sv = reinterpret_cast<const float2*>(dsc + t * nbp)[qp];
+            sa[t] = sv.x;
+            sb[t] = sv.y;
+        }
+        float res[UPW][TC][NR];
 #pragma unroll
         for (int u = 0; u < UPW; ++u) {
-            const int row = (unit0 + u) * RPS + g;
+            const int lr = u * RPS + g;           // row within the wave's span
+            float acc[NR][TC];
 #pragma unroll
-            for (int t = 0; t < TC; ++t) {
-                float v[NR];
+            for (int r = 0; r < NR; ++r) {
+                const int nh = lr < nrows ? nblk_here : 0;
+                const int off = loff[r] + lr * (int)row_bytes + 36 * q;
+                const PairDec w = lds_pair<EVEN_NB>(wl + r * (span_bytes + 16) + (nh > 0 ? off : 0), nh);
 #pragma unroll
-                for (int r = 0; r < NR; ++r) v[r] = group_sum<LPR>(acc[u][r][t]);
-                if (q == 0 && row < rows_out && c0 + t < ne_tok) {
-                    const int64_t p = p0 + c0 + t;
-                    if (MODE == 0) {
-                        store_act(out, ADT, p * I + row, gelu_tanh(v[0]) * v[NR - 1]);
-                    } else {
-                        reinterpret_cast<float*>(out)[p * H + row] = v[0];
+                for (int t = 0; t < TC; ++t) {
+                    const int ia = block_idot(w.qA, xa[t]);
+                    const int ib = block_idot(w.qB, xb[t]);
+                    acc[r][t] = fmaf(w.dA * sa[t], (float)ia, (w.dB * sb[t]) * (float)ib);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < TC; ++t)
+#pragma unroll
+                for (int r = 0; r < NR; ++r) res[u][t][r] = group_sum<LPR>(acc[r][t]);
+        }
+        if (LPR == 64) {
+            // one row per step: every sum sits in lane 63; spread them so that lane
+            // u*TC + t finishes (u, t) and the GELU evaluations run side by side
+            float mine[NR];
+#pragma unroll
+            for (int r = 0; r < NR; ++r) mine[r] = 0.f;
+#pragma unroll
+            for (int u = 0; u < UPW; ++u)
+#pragma unroll
+                for (int t = 0; t < TC; ++t)
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) {
+                        const float v = __int_as_float(
+                            __builtin_amdgcn_readlane(__float_as_int(res[u][t][r]), 63));
+                        if (lane == u * TC + t) mine[r] = v;
+                    }
+            const int u = lane / TC, t = lane % TC;
+            if (lane < UPW * TC && u < nrows && c0 + t < ne_tok) {
+                const int64_t p = p0 + c0 + t;
+                const int row = row0 + u;
+                if (MODE == 0)
+                    store_act(out, ADT, p * I + row, gelu_tanh(mine[0]) * mine[NR - 1]);
+                else
+                    reinterpret_cast<float*>(out)[p * H + row] = mine[0];
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < UPW; ++u) {
+                const int lr = u * RPS + g;
+#pragma unroll
+                for (int t = 0; t < TC; ++t) {
+                    if (q == LPR - 1 && lr < nrows && c0 + t < ne_tok) {
+                        const int64_t p = p0 + c0 + t;
+                        const int row = row0 + lr;
+                        if (MODE == 0)
+                            store_act(out, ADT, p * I + row,
+                                      gelu_tanh(res[u][t][0]) * res[u][t][NR - 1]);
+                        else
+                            reinterpret_cast<float*>(out)[p * H + row] = res[u][t][0];
                     }
                 }
             }
         }
+    };
+    digitize(0);
+    compute(0);
+    for (int c0 = TC; c0 < ne_tok; c0 += TC) {
+        __syncthreads();  // digits of the previous chunk are no longer read
+        load_x(c0);
+        digitize(c0);
+        compute(c0);
     }
 }
 
 // ---- dispatch ---------------------------------------------------------------------
-template <int MODE, int ADT, int LPR>
+template <int MODE, int ADT, int LPR, int TC, bool EVEN_NB>
 static void launch_mode(const uint8_t* W, int nb, int I, int H, const void* act,
                         const int32_t* offsets, const int32_t* sorted_slots, int K, int E,
                         int n_active, void* out, hipStream_t st) {
-    constexpr int TC = 2, UPW = 4, RPS = 64 / LPR;
+    constexpr int RPS = 64 / LPR;
+    constexpr int UPW = (MODE == 0) ? (RPS >= 2 ? 1 : 2 / RPS) : (RPS >= 8 ? 1 : 8 / RPS);
+    constexpr int RPW = RPS * UPW;
+    constexpr int NR = (MODE == 0) ? 2 : 1;
     const int rows_out = (MODE == 0) ? I : H;
-    const int units = (rows_out + RPS - 1) / RPS;
-    const int wgs = (units + 4 * UPW - 1) / (4 * UPW);
-    const size_t lds = (size_t)TC * nb * 17 * sizeof(uint32_t);
+    const int wgs = (rows_out + 4 * RPW - 1) / (4 * RPW);
+    constexpr int NCH = (RPW * 36 * LPR + 15 + 1023) / 1024;
+    const int wave_lds = NR * NCH * 1024;
+    const size_t lds = (size_t)4 * wave_lds + (size_t)TC * ((nb + 1) & ~1) * 17 * sizeof(uint32_t);
     dim3 grid(wgs, n_active);
-    ffn_gemv_q4_0<MODE, ADT, LPR, TC, UPW><<<grid, 256, lds, st>>>(W, nb, I, H, act, offsets,
-                                                                   sorted_slots, K, E, out);
+    ffn_gemv_q4_0<MODE, ADT, LPR, TC, UPW, EVEN_NB><<<grid, 256, lds, st>>>(
+        W, nb, I, H, act, offsets, sorted_slots, K, E, out, wave_lds);
 }
 
-template <int MODE, int ADT>
+template <int MODE, int ADT, int TC>
 static void launch_lpr(const uint8_t* W, int nb, int I, int H, const void* act,
                        const int32_t* offsets, const int32_t* sorted_slots, int K, int E,
                        int n_active, void* out, hipStream_t st) {
     const int pairs = (nb + 1) / 2;
-#define MOE_LPR_CASE(L)                                                                        \
-    if (pairs <= L) {                                                                          \
-        launch_mode<MODE, ADT, L>(W, nb, I, H, act, offsets, sorted_slots, K, E, n_active, out, \
-                                  st);                                                         \
-        return;                                                                                \
+#define MOE_LPR_CASE(L)                                                                         \
+    if (pairs <= L) {                                                                           \
+        if (nb & 1)                                                                             \
+            launch_mode<MODE, ADT, L, TC, false>(W, nb, I, H, act, offsets, sorted_slots, K, E, \
+                                                 n_active, out, st);                            \
+        else                                                                                    \
+            launch_mode<MODE, ADT, L, TC, true>(W, nb, I, H, act, offsets, sorted_slots, K, E,  \
+                                                n_active, out, st);                             \
+        return;                                                                                 \
     }
     MOE_LPR_CASE(1) MOE_LPR_CASE(2) MOE_LPR_CASE(4) MOE_LPR_CASE(8) MOE_LPR_CASE(16)
     MOE_LPR_CASE(32) MOE_LPR_CASE(64)
 #undef MOE_LPR_CASE
 }
 
-hipError_t launch_ffn_gemv(const void* x, int x_dt, int H, const uint8_t* w_gate_up,
+template <int ADT, int TC>
+static void launch_both(const void* x, int H, const uint8_t* w_gate_up, const uint8_t* w_down,
+                        int I, int E, int K, int n_active, const int32_t* offsets,
+                        const int32_t* sorted_slots, void* h_ws, float* y_sorted, hipStream_t st) {
+    launch_lpr<0, ADT, TC>(w_gate_up, H / 32, I, H, x, offsets, sorted_slots, K, E, n_active, h_ws,
+                           st);
+    launch_lpr<1, ADT, TC>(w_down, I / 32, I, H, h_ws, offsets, sorted_slots, K, E, n_active,
+                           y_sorted, st);
+}
+
+hipError_t launch_ffn_gemv(const void* x, int x_dt, int64_t T, int H, const uint8_t* w_gate_up,
                            const uint8_t* w_down, int I, int E, int K, int N,
                            const int32_t* offsets, const int32_t* sorted_slots, void* h_ws,
                            float* y_sorted, hipStream_t st) {
     const int n_active = min(E, N);
+    // tokens per expert never exceed T: one token per chunk when T == 1
     if (x_dt == MOE_F32) {
-        launch_lpr<0, MOE_F32>(w_gate_up, H / 32, I, H, x, offsets, sorted_slots, K, E, n_active,
-                               h_ws, st);
-        launch_lpr<1, MOE_F32>(w_down, I / 32, I, H, h_ws, offsets, sorted_slots, K, E, n_active,
-                               y_sorted, st);
+        if (T == 1)
+            launch_both<MOE_F32, 1>(x, H, w_gate_up, w_down, I, E, K, n_active, offsets,
+                                    sorted_slots, h_ws, y_sorted, st);
+        else
+            launch_both<MOE_F32, 2>(x, H, w_gate_up, w_down, I, E, K, n_active, offsets,
+                                    sorted_slots, h_ws, y_sorted, st);
     } else {
-        launch_lpr<0, MOE_BF16>(w_gate_up, H / 32, I, H, x, offsets, sorted_slots, K, E, n_active,
-                                h_ws, st);
-        launch_lpr<1, MOE_BF16>(w_down, I / 32, I, H, h_ws, offsets, sorted_slots, K, E, n_active,
-                                y_sorted, st);
+        if (T == 1)
+            launch_both<MOE_BF16, 1>(x, H, w_gate_up, w_down, I, E, K, n_active, offsets,
+                                     sorted_slots, h_ws, y_sorted, st);
+        else
+            launch_both<MOE_BF16, 2>(x, H, w_gate_up, w_down, I, E, K, n_active, offsets,
+                                     sorted_slots, h_ws, y_sorted, st);
     }
     return hipGetLastError();
 }

@@ -19,7 +19,7 @@ size_t permute_ws_bytes(int64_t N, int E);
 hipError_t launch_permute(const int32_t* ids, int N, int E, int32_t* offsets, int32_t* sorted_slots,
                           int32_t* slot_pos, void* ws, hipStream_t st);
 
-hipError_t launch_ffn_gemv(const void* x, int x_dt, int H, const uint8_t* w_gate_up,
+hipError_t launch_ffn_gemv(const void* x, int x_dt, int64_t T, int H, const uint8_t* w_gate_up,
                            const uint8_t* w_down, int I, int E, int K, int N,
                            const int32_t* offsets, const int32_t* sorted_slots, void* h_ws,
                            float* y_sorted, hipStream_t st);

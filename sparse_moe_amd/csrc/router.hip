@@ -9,8 +9,17 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Few tokens: one wave per expert streams its W_r row once (float4 loads) and
-// dots it with every token (T <= ROUTER_GEMV_MAX_T).
+// Few tokens: one wave per expert streams its W_r row once (float4 loads, all
+// issued at once) and dots it with every token (T <= ROUTER_GEMV_MAX_T).
+constexpr int ROUTER_MAX_CHUNKS = MOE_MAX_H / 256;  // float4 chunks of 64 lanes per row
+
+MOE_DEV float4 load_x4(const void* x, int xdt, int64_t i4) {
+    if (xdt == MOE_F32) return reinterpret_cast<const float4*>(x)[i4];
+    const uint2 b = reinterpret_cast<const uint2*>(x)[i4];
+    return make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
+                       __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
+}
+
 template <int XDT>
 __global__ __launch_bounds__(256) void router_logits_gemv(const void* __restrict__ x, int T, int H,
                                                           const float* __restrict__ W,
@@ -21,39 +30,34 @@ __global__ __launch_bounds__(256) void router_logits_gemv(const void* __restrict
     const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (e >= E) return;
     const float* w = W + (int64_t)e * H;
-    float acc[ROUTER_GEMV_MAX_T];
-#pragma unroll
-    for (int t = 0; t < ROUTER_GEMV_MAX_T; ++t) acc[t] = 0.f;
     const int H4 = H >> 2;
-    for (int j4 = lane; j4 < H4; j4 += 64) {
-        const float4 wv = reinterpret_cast<const float4*>(w)[j4];
-        float4 sv = make_float4(1.f, 1.f, 1.f, 1.f);
-        if (rsc) sv = reinterpret_cast<const float4*>(rsc)[j4];
+    float4 wv[ROUTER_MAX_CHUNKS];
 #pragma unroll
-        for (int t = 0; t < ROUTER_GEMV_MAX_T; ++t) {
-            if (t < T) {
-                float4 xv;
-                if (XDT == MOE_F32) {
-                    xv = reinterpret_cast<const float4*>(x)[(int64_t)t * H4 + j4];
-                } else {
-                    const uint2 b = reinterpret_cast<const uint2*>(x)[(int64_t)t * H4 + j4];
-                    xv = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
-                                     __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
-                }
-                acc[t] += (xv.x * sv.x) * wv.x;
-                acc[t] += (xv.y * sv.y) * wv.y;
-                acc[t] += (xv.z * sv.z) * wv.z;
-                acc[t] += (xv.w * sv.w) * wv.w;
-            }
+    for (int c = 0; c < ROUTER_MAX_CHUNKS; ++c) {
+        const int j4 = min(lane + 64 * c, H4 - 1);
+        wv[c] = reinterpret_cast<const float4*>(w)[j4];
+        if (lane + 64 * c >= H4) wv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (rsc) {
+#pragma unroll
+        for (int c = 0; c < ROUTER_MAX_CHUNKS; ++c) {
+            const float4 sv = reinterpret_cast<const float4*>(rsc)[min(lane + 64 * c, H4 - 1)];
+            wv[c].x *= sv.x; wv[c].y *= sv.y; wv[c].z *= sv.z; wv[c].w *= sv.w;
         }
     }
     const float b = bias ? bias[e] : 0.f;
+    for (int t = 0; t < T; ++t) {
+        float acc = 0.f;
 #pragma unroll
-    for (int t = 0; t < ROUTER_GEMV_MAX_T; ++t) {
-        if (t < T) {
-            const float s = wave_sum(acc[t]);
-            if (lane == 0) logits[(int64_t)t * E + e] = s + b;
+        for (int c = 0; c < ROUTER_MAX_CHUNKS; ++c) {
+            const float4 xv = load_x4(x, XDT, (int64_t)t * H4 + min(lane + 64 * c, H4 - 1));
+            acc = fmaf(xv.x, wv[c].x, acc);
+            acc = fmaf(xv.y, wv[c].y, acc);
+            acc = fmaf(xv.z, wv[c].z, acc);
+            acc = fmaf(xv.w, wv[c].w, acc);
         }
+        const float s = wave_sum(acc);
+        if (lane == 0) logits[(int64_t)t * E + e] = s + b;
     }
 }
 
@@ -126,7 +130,10 @@ __global__ __launch_bounds__(256) void router_logits_tiled(const void* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Top-K: one wave per token; each lane holds experts lane, lane+64, ...
+// Top-K: one wave per token; lane l holds the logits of experts l, l+64, l+128,
+// l+192.  Each of the K rounds takes the wave maximum (DPP) of the untaken
+// logits and the lowest expert index holding it (ballots), so equal logits
+// go in ascending expert order.
 __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ logits, int64_t T,
                                                     int E, int K, int32_t* __restrict__ ids,
                                                     float* __restrict__ w) {
@@ -138,9 +145,11 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ lo
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = lane + 64 * i;
-        v[i] = e < E ? l[e] : 0.f;
+        v[i] = e < E ? l[e] + 0.f : -INFINITY;  // + 0 turns -0 into +0
     }
-    uint32_t taken = 0;
+    bool live[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) live[i] = lane + 64 * i < E;
     float selv[MOE_MAX_K];
     int seli[MOE_MAX_K];
 #pragma unroll
@@ -148,28 +157,25 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ lo
         selv[k] = 0.f;
         seli[k] = 0;
         if (k < K) {
-            float bv = -INFINITY;
-            int bi = 0x7FFFFFFF;
+            float m = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (live[i]) m = fmaxf(m, v[i]);
+            m = wave_max(m);
+            int idx = -1;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int e = lane + 64 * i;
-                if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
-                    bv = v[i];
-                    bi = e;
-                }
+                const uint64_t bal = __ballot(live[i] && v[i] == m);
+                if (idx < 0 && bal) idx = 64 * i + (int)__builtin_ctzll(bal);
             }
+            if (idx < 0) idx = 0;  // only when every remaining logit is NaN
+            selv[k] = m;
+            seli[k] = idx;
+            if ((idx & 63) == lane) {
 #pragma unroll
-            for (int m = 32; m >= 1; m >>= 1) {
-                const float ov = __shfl_xor(bv, m, 64);
-                const int oi = __shfl_xor(bi, m, 64);
-                if (ov > bv || (ov == bv && oi < bi)) {
-                    bv = ov;
-                    bi = oi;
-                }
+                for (int i = 0; i < 4; ++i)
+                    if (i == (idx >> 6)) live[i] = false;
             }
-            selv[k] = bv;
-            seli[k] = bi;
-            if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
         }
     }
     float s = 0.f;
