@@ -112,6 +112,25 @@ moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E,
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Routing in one call: moe_router_topk followed by moe_permute, with the same
+ * results (same arguments as those two calls; W_r == NULL again selects
+ * injected logits).  For T <= 8 and a router weight, one kernel does all of it:
+ * every workgroup computes a share of the router logits and the last one to
+ * finish (counted by an atomic in the workspace) runs top-K and the
+ * permutation.  This is the decode path; it saves two kernel boundaries.
+ *
+ *   ws   device workspace of at least moe_route_workspace_bytes(T, K, E) bytes,
+ *        ZERO-FILLED before its first use; every call leaves it zero-filled
+ *        again.  Calls sharing a workspace must be ordered on one stream.
+ */
+size_t moe_route_workspace_bytes(int64_t T, int32_t K, int32_t E);
+moe_status moe_route(const void* x, int x_dt, int64_t T, int32_t H, const float* W_r,
+                     const float* r_scale, const float* logit_bias, int32_t E, int32_t K,
+                     float* logits, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                     int32_t* sorted_slots, int32_t* slot_pos, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/*
  * Expert FFN on Q4_0 weights read in place (model card intro: the release's
  * ggml blocks are kept byte for byte and multiplied in place; table "What is
  * inside": expert-major [gate; up] 2 x I rows and down H rows).

@@ -30,6 +30,9 @@ SIGNATURES = {
     "moe_abi_version": ([], C.c_int),
     "moe_router_topk": ([_P, C.c_int, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _P, _P, _P], C.c_int),
     "moe_permute_workspace_bytes": ([_I64, _I32, _I32], _SZ),
+    "moe_route_workspace_bytes": ([_I64, _I32, _I32], _SZ),
+    "moe_route": ([_P, C.c_int, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                   _P], C.c_int),
     "moe_permute": ([_P, _I64, _I32, _I32, _P, _P, _P, _P, _SZ, _P], C.c_int),
     "moe_expert_ffn_q4_0_workspace_bytes": ([_I64, _I32, _I32, _I32, _I32, C.c_int], _SZ),
     "moe_expert_ffn_q4_0": ([_P, C.c_int, _I64, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P,
@@ -134,6 +137,36 @@ def moe_permute(topk_ids: torch.Tensor, E: int, expert_offsets: torch.Tensor,
                            _ptr(slot_pos), _ptr(ws), nbytes, _stream(stream)), "moe_permute")
 
 
+def moe_route_workspace_bytes(T: int, K: int, E: int) -> int:
+    return lib.moe_route_workspace_bytes(T, K, E)
+
+
+def moe_route(x: Optional[torch.Tensor], W_r: Optional[torch.Tensor], logits: torch.Tensor,
+              topk_ids: torch.Tensor, topk_w: torch.Tensor, expert_offsets: torch.Tensor,
+              sorted_slots: torch.Tensor, slot_pos: torch.Tensor, ws: torch.Tensor, r_scale=None,
+              logit_bias=None, stream=None):
+    """Router + top-K + permutation (ws zero-filled before first use)."""
+    T, E = logits.shape
+    K = topk_ids.shape[1]
+    H = 0 if W_r is None else W_r.shape[1]
+    for t, n, d in ((x, "x", None), (W_r, "W_r", torch.float32), (logits, "logits", torch.float32),
+                    (topk_ids, "topk_ids", torch.int32), (topk_w, "topk_w", torch.float32),
+                    (r_scale, "r_scale", torch.float32), (logit_bias, "logit_bias", torch.float32),
+                    (expert_offsets, "expert_offsets", torch.int32),
+                    (sorted_slots, "sorted_slots", torch.int32), (slot_pos, "slot_pos", torch.int32),
+                    (ws, "ws", None)):
+        _dev(t, n, d)
+    if W_r is not None and (x is None or tuple(x.shape) != (T, H) or W_r.shape[0] != E):
+        raise ValueError("router shapes disagree")
+    if expert_offsets.numel() != E + 1 or sorted_slots.numel() != T * K or slot_pos.numel() != T * K:
+        raise ValueError("permutation output sizes disagree")
+    xdt = act_dtype(x) if x is not None else MOE_F32
+    _check(lib.moe_route(_ptr(x), xdt, T, H, _ptr(W_r), _ptr(r_scale), _ptr(logit_bias), E, K,
+                         _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets),
+                         _ptr(sorted_slots), _ptr(slot_pos), _ptr(ws), ws.numel() * ws.element_size(),
+                         _stream(stream)), "moe_route")
+
+
 def moe_expert_ffn_q4_0_workspace_bytes(T: int, K: int, H: int, I: int, E: int, x_dt: int) -> int:
     return lib.moe_expert_ffn_q4_0_workspace_bytes(T, K, H, I, E, x_dt)
 
@@ -213,13 +246,18 @@ class LayerBuffers:
         pb = max(16, moe_permute_workspace_bytes(T, K, E))
         fb = max(16, moe_expert_ffn_q4_0_workspace_bytes(T, K, H, I, E, xdt))
         self.ws_perm = torch.empty((pb,), dtype=torch.uint8, device=device)
+        rb = moe_route_workspace_bytes(T, K, E)
+        self.ws_route = torch.zeros((max(16, rb),), dtype=torch.uint8, device=device)
         self.ws_ffn = torch.empty((fb,), dtype=torch.uint8, device=device)
 
 
 def moe_layer(x, W_r, w_gate_up, w_down, K, expert_scale=None, logit_bias=None, r_scale=None,
               bufs: Optional[LayerBuffers] = None, logits_in=None, out_act=None, residual=None,
-              stream=None) -> LayerBuffers:
-    """One routed-MoE layer: router/top-K -> permute -> expert FFN -> combine."""
+              fused_route: bool = False, stream=None) -> LayerBuffers:
+    """One routed-MoE layer: router/top-K -> permute -> expert FFN -> combine.
+
+    fused_route: use moe_route (one call for routing and permutation) instead
+    of moe_router_topk + moe_permute."""
     T, H = x.shape
     E = w_gate_up.shape[0]
     I = w_gate_up.shape[1] // 2
@@ -227,12 +265,16 @@ def moe_layer(x, W_r, w_gate_up, w_down, K, expert_scale=None, logit_bias=None, 
         bufs = LayerBuffers(T, H, I, E, K, x.dtype, device=x.device)
     if logits_in is not None:
         bufs.logits.copy_(logits_in)
-        moe_router_topk(None, None, bufs.logits, bufs.topk_ids, bufs.topk_w, stream=stream)
+    xr, wr = (None, None) if logits_in is not None else (x, W_r)
+    if fused_route:
+        moe_route(xr, wr, bufs.logits, bufs.topk_ids, bufs.topk_w, bufs.offsets, bufs.sorted_slots,
+                  bufs.slot_pos, bufs.ws_route, r_scale=r_scale, logit_bias=logit_bias,
+                  stream=stream)
     else:
-        moe_router_topk(x, W_r, bufs.logits, bufs.topk_ids, bufs.topk_w, r_scale=r_scale,
+        moe_router_topk(xr, wr, bufs.logits, bufs.topk_ids, bufs.topk_w, r_scale=r_scale,
                         logit_bias=logit_bias, stream=stream)
-    moe_permute(bufs.topk_ids, E, bufs.offsets, bufs.sorted_slots, bufs.slot_pos, bufs.ws_perm,
-                stream=stream)
+        moe_permute(bufs.topk_ids, E, bufs.offsets, bufs.sorted_slots, bufs.slot_pos,
+                    bufs.ws_perm, stream=stream)
     moe_expert_ffn_q4_0(x, w_gate_up, w_down, K, bufs.offsets, bufs.sorted_slots, bufs.y_sorted,
                         bufs.ws_ffn, stream=stream)
     moe_combine(bufs.y_sorted, bufs.slot_pos, bufs.topk_ids, bufs.topk_w, expert_scale,

@@ -85,6 +85,49 @@ moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E,
                                           slot_pos, ws, (hipStream_t)stream));
 }
 
+size_t moe_route_workspace_bytes(int64_t T, int32_t K, int32_t E) {
+    if (check_ekh(T, K, E) != MOE_OK) return 0;
+    // [0, 256): completion counter of the fused few-token kernel; then the
+    // workspace of the multi-tile permutation
+    return 256 + round_up(moe::permute_ws_bytes(T * K, E), 256);
+}
+
+moe_status moe_route(const void* x, int x_dt, int64_t T, int32_t H, const float* W_r,
+                     const float* r_scale, const float* logit_bias, int32_t E, int32_t K,
+                     float* logits, int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                     int32_t* sorted_slots, int32_t* slot_pos, void* ws, size_t ws_bytes,
+                     void* stream) {
+    moe_status s = check_ekh(T, K, E);
+    if (s != MOE_OK) return s;
+    if (W_r && (s = check_dim(H, MOE_MAX_H)) != MOE_OK) return s;
+    if (!dtype_ok(x_dt)) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_w || (W_r && !x) || !expert_offsets || !sorted_slots ||
+        !slot_pos)
+        return MOE_ERR_NULL;
+    if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w) ||
+        !aligned16(expert_offsets) || !aligned16(sorted_slots) || !aligned16(slot_pos))
+        return MOE_ERR_ALIGN;
+    if (W_r && (!aligned16(x) || !aligned16(W_r) || (r_scale && !aligned16(r_scale)) ||
+                (logit_bias && !aligned16(logit_bias))))
+        return MOE_ERR_ALIGN;
+    const size_t need = moe_route_workspace_bytes(T, K, E);
+    if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    const int N = (int)(T * K);
+    if (W_r && T <= moe::ROUTER_GEMV_MAX_T && N <= moe::PERM_TILE)
+        return hip_status(moe::launch_route_small(x, x_dt, (int)T, H, W_r, r_scale, logit_bias, E, K,
+                                                  logits, topk_ids, topk_w, expert_offsets,
+                                                  sorted_slots, slot_pos, (int*)ws, st));
+    if (W_r && (s = hip_status(moe::launch_router_logits(x, x_dt, T, H, W_r, r_scale, logit_bias, E,
+                                                        logits, st))) != MOE_OK)
+        return s;
+    if ((s = hip_status(moe::launch_topk(logits, T, E, K, topk_ids, topk_w, st))) != MOE_OK) return s;
+    return hip_status(moe::launch_permute(topk_ids, N, E, expert_offsets, sorted_slots, slot_pos,
+                                          (uint8_t*)ws + 256, st));
+}
+
 size_t moe_expert_ffn_q4_0_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_t I, int32_t E,
                                            int x_dt) {
     if (check_ekh(T, K, E) != MOE_OK || check_dim(H, MOE_MAX_H) != MOE_OK ||

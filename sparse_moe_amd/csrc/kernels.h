@@ -12,6 +12,10 @@ constexpr int DIGIT_NMAX = 30583;      // largest |n| with 4 balanced base-16 di
 hipError_t launch_router_logits(const void* x, int x_dt, int64_t T, int H, const float* W,
                                 const float* rsc, const float* bias, int E, float* logits,
                                 hipStream_t st);
+hipError_t launch_route_small(const void* x, int x_dt, int T, int H, const float* W,
+                              const float* rsc, const float* bias, int E, int K, float* logits,
+                              int32_t* ids, float* w, int32_t* offsets, int32_t* sorted_slots,
+                              int32_t* slot_pos, int* counter, hipStream_t st);
 hipError_t launch_topk(const float* logits, int64_t T, int E, int K, int32_t* ids, float* w,
                        hipStream_t st);
 

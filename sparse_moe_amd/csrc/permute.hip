@@ -7,68 +7,27 @@
 // One tile: a single workgroup finishes the sort.  Several tiles: per-tile
 // counts -> one scan workgroup (prefix over tiles, then over experts) ->
 // scatter.  No atomics; the result is unique.
-#include "kernels.h"
+#include "route_dev.h"
 
 namespace moe {
 
-MOE_DEV uint64_t lanemask_lt() {
-    const int l = __lane_id();
-    return l == 0 ? 0ull : (~0ull >> (64 - l));
+// One tile: a single workgroup sorts every slot.
+__global__ __launch_bounds__(256) void permute_single(const int32_t* __restrict__ ids, int N, int E,
+                                                      int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ sorted_slots,
+                                                      int32_t* __restrict__ slot_pos) {
+    permute_block(ids, N, E, offsets, sorted_slots, slot_pos);
 }
 
-// mask of the lanes of this wave whose key equals mine (keys < 512)
-MOE_DEV uint64_t match_key9(uint32_t key) {
-    uint64_t m = ~0ull;
-#pragma unroll
-    for (int b = 0; b < 9; ++b) {
-        const uint32_t bit = (key >> b) & 1u;
-        const uint64_t bal = __ballot(bit);
-        m &= bit ? bal : ~bal;
-    }
-    return m;
-}
-
-// Exclusive scan of cnt[0..n) (n <= 256) into out[0..n], out[n] = total, by 256 threads.
-MOE_DEV void block_exclusive_scan256(const int* cnt, int n, int* tmp, int32_t* out_global,
-                                     int* out_lds) {
-    const int tid = threadIdx.x;
-    int v = tid < n ? cnt[tid] : 0;
-    tmp[tid] = v;
-    __syncthreads();
-    for (int d = 1; d < 256; d <<= 1) {
-        const int a = tid >= d ? tmp[tid - d] : 0;
-        __syncthreads();
-        tmp[tid] += a;
-        __syncthreads();
-    }
-    const int incl = tmp[tid];
-    if (tid < n) {
-        if (out_global) out_global[tid] = incl - v;
-        if (out_lds) out_lds[tid] = incl - v;
-    }
-    if (tid == n - 1) {
-        if (out_global) out_global[n] = incl;
-        if (out_lds) out_lds[n] = incl;
-    }
-    __syncthreads();
-}
-
-// Per-tile stable ranks.  SINGLE: the only tile; finish the sort here.
-template <bool SINGLE>
+// Several tiles: per-tile stable ranks and per-expert tile counts.
 __global__ __launch_bounds__(256) void permute_tiles(const int32_t* __restrict__ ids, int N, int E,
                                                      int32_t* __restrict__ tile_counts,
-                                                     int32_t* __restrict__ local_rank,
-                                                     int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ sorted_slots,
-                                                     int32_t* __restrict__ slot_pos) {
+                                                     int32_t* __restrict__ local_rank) {
     __shared__ int run[MOE_MAX_E];
     __shared__ int wcnt[4][MOE_MAX_E];
-    __shared__ int tmp[256];
-    __shared__ int off[MOE_MAX_E + 1];
     const int tid = threadIdx.x, wave = tid >> 6;
     run[tid] = 0;  // blockDim == MOE_MAX_E
     const int base = blockIdx.x * PERM_TILE;
-    int rank[PERM_TILE / 256], ex[PERM_TILE / 256];
 #pragma unroll
     for (int r = 0; r < PERM_TILE / 256; ++r) {
         const int s = base + r * 256 + tid;
@@ -82,36 +41,16 @@ __global__ __launch_bounds__(256) void permute_tiles(const int32_t* __restrict__
         const int rw = __popcll(m & lanemask_lt());
         if (valid && rw == 0) wcnt[wave][e] = __popcll(m);
         __syncthreads();
-        int rk = rw;
         if (valid) {
-            rk += run[e];
+            int rk = rw + run[e];
             for (int w = 0; w < wave; ++w) rk += wcnt[w][e];
+            local_rank[s] = rk;
         }
-        rank[r] = rk;
-        ex[r] = valid ? e : -1;
         __syncthreads();
         run[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
         __syncthreads();
     }
-    if (!SINGLE) {
-#pragma unroll
-        for (int r = 0; r < PERM_TILE / 256; ++r) {
-            const int s = base + r * 256 + tid;
-            if (ex[r] >= 0) local_rank[s] = rank[r];
-        }
-        if (tid < E) tile_counts[(int64_t)blockIdx.x * E + tid] = run[tid];
-    } else {
-        block_exclusive_scan256(run, E, tmp, offsets, off);
-#pragma unroll
-        for (int r = 0; r < PERM_TILE / 256; ++r) {
-            const int s = base + r * 256 + tid;
-            if (ex[r] >= 0) {
-                const int pos = off[ex[r]] + rank[r];
-                sorted_slots[pos] = s;
-                slot_pos[s] = pos;
-            }
-        }
-    }
+    if (tid < E) tile_counts[(int64_t)blockIdx.x * E + tid] = run[tid];
 }
 
 // One workgroup: per-expert prefix over tiles (tile_base), then expert offsets.
@@ -174,16 +113,14 @@ size_t permute_ws_bytes(int64_t N, int E) {
 hipError_t launch_permute(const int32_t* ids, int N, int E, int32_t* offsets, int32_t* sorted_slots,
                           int32_t* slot_pos, void* ws, hipStream_t st) {
     if (N <= PERM_TILE) {
-        permute_tiles<true><<<1, 256, 0, st>>>(ids, N, E, nullptr, nullptr, offsets, sorted_slots,
-                                                slot_pos);
+        permute_single<<<1, 256, 0, st>>>(ids, N, E, offsets, sorted_slots, slot_pos);
         return hipGetLastError();
     }
     const int ntiles = (N + PERM_TILE - 1) / PERM_TILE;
     int32_t* tile_counts = (int32_t*)ws;
     int32_t* tile_base = tile_counts + (int64_t)ntiles * E;
     int32_t* local_rank = tile_base + (int64_t)ntiles * E;
-    permute_tiles<false><<<ntiles, 256, 0, st>>>(ids, N, E, tile_counts, local_rank, nullptr, nullptr,
-                                                 nullptr);
+    permute_tiles<<<ntiles, 256, 0, st>>>(ids, N, E, tile_counts, local_rank);
     permute_scan<<<1, 256, 0, st>>>(ntiles, E, tile_counts, tile_base, offsets);
     permute_scatter<<<ntiles, 256, 0, st>>>(ids, N, E, tile_base, local_rank, offsets, sorted_slots,
                                             slot_pos);

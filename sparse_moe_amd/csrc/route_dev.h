@@ -1,0 +1,160 @@
+// Device helpers shared by the routing kernels (router top-K, permutation).
+#pragma once
+
+#include "kernels.h"
+
+namespace moe {
+
+MOE_DEV uint64_t lanemask_lt() {
+    const int l = __lane_id();
+    return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// mask of the lanes of this wave whose key equals mine (keys < 512)
+MOE_DEV uint64_t match_key9(uint32_t key) {
+    uint64_t m = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 9; ++b) {
+        const uint32_t bit = (key >> b) & 1u;
+        const uint64_t bal = __ballot(bit);
+        m &= bit ? bal : ~bal;
+    }
+    return m;
+}
+
+// Exclusive scan of cnt[0..n) (n <= 256) into out[0..n], out[n] = total, by 256 threads.
+MOE_DEV void block_exclusive_scan256(const int* cnt, int n, int* tmp, int32_t* out_global,
+                                     int* out_lds) {
+    const int tid = threadIdx.x;
+    int v = tid < n ? cnt[tid] : 0;
+    tmp[tid] = v;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+        const int a = tid >= d ? tmp[tid - d] : 0;
+        __syncthreads();
+        tmp[tid] += a;
+        __syncthreads();
+    }
+    const int incl = tmp[tid];
+    if (tid < n) {
+        if (out_global) out_global[tid] = incl - v;
+        if (out_lds) out_lds[tid] = incl - v;
+    }
+    if (tid == n - 1) {
+        if (out_global) out_global[n] = incl;
+        if (out_lds) out_lds[n] = incl;
+    }
+    __syncthreads();
+}
+
+
+// Stable counting sort of N <= PERM_TILE slots by one workgroup of 256 threads
+// (4 rounds of 256 slots): stable ranks from the wave match plus per-wave
+// counts, then offsets by a block scan, then the scatter.
+MOE_DEV void permute_block(const int32_t* ids, int N, int E, int32_t* offsets,
+                           int32_t* sorted_slots, int32_t* slot_pos) {
+    __shared__ int run[MOE_MAX_E];
+    __shared__ int wcnt[4][MOE_MAX_E];
+    __shared__ int tmp[256];
+    __shared__ int off[MOE_MAX_E + 1];
+    const int tid = threadIdx.x, wave = tid >> 6;
+    run[tid] = 0;  // blockDim == MOE_MAX_E
+    int rank[PERM_TILE / 256], ex[PERM_TILE / 256];
+#pragma unroll
+    for (int r = 0; r < PERM_TILE / 256; ++r) {
+        const int s = r * 256 + tid;
+        const bool valid = s < N;
+        const int e = valid ? ids[s] : 0;
+        const uint32_t key = valid ? (uint32_t)e : 256u;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
+        __syncthreads();
+        const uint64_t m = match_key9(key);
+        const int rw = __popcll(m & lanemask_lt());
+        if (valid && rw == 0) wcnt[wave][e] = __popcll(m);
+        __syncthreads();
+        int rk = rw;
+        if (valid) {
+            rk += run[e];
+            for (int w = 0; w < wave; ++w) rk += wcnt[w][e];
+        }
+        rank[r] = rk;
+        ex[r] = valid ? e : -1;
+        __syncthreads();
+        run[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
+        __syncthreads();
+    }
+    block_exclusive_scan256(run, E, tmp, offsets, off);
+#pragma unroll
+    for (int r = 0; r < PERM_TILE / 256; ++r) {
+        const int s = r * 256 + tid;
+        if (ex[r] >= 0) {
+            const int pos = off[ex[r]] + rank[r];
+            sorted_slots[pos] = s;
+            slot_pos[s] = pos;
+        }
+    }
+}
+
+// Top-K of one token's E logits by one wave; lane l holds experts l, l+64,
+// l+128, l+192.  Each of the K rounds takes the wave maximum (DPP) of the
+// untaken logits and the lowest expert index holding it (ballots), so equal
+// logits go in ascending expert order.  Weights: softmax over the K kept
+// logits.  Every lane of the wave must be active.
+MOE_DEV void topk_token(const float* l, int E, int K, int32_t* ids, float* w) {
+    const int lane = threadIdx.x & 63;
+    float v[4];
+    bool live[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        live[i] = e < E;
+        v[i] = live[i] ? l[e] + 0.f : -INFINITY;  // + 0 turns -0 into +0
+    }
+    float selv[MOE_MAX_K];
+    int seli[MOE_MAX_K];
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_K; ++k) {
+        selv[k] = 0.f;
+        seli[k] = 0;
+        if (k < K) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (live[i]) m = fmaxf(m, v[i]);
+            m = wave_max(m);
+            int idx = -1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint64_t bal = __ballot(live[i] && v[i] == m);
+                if (idx < 0 && bal) idx = 64 * i + (int)__builtin_ctzll(bal);
+            }
+            if (idx < 0) idx = 0;  // only when every remaining logit is NaN
+            selv[k] = m;
+            seli[k] = idx;
+            if ((idx & 63) == lane) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (i == (idx >> 6)) live[i] = false;
+            }
+        }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_K; ++k)
+        if (k < K) s += expf(selv[k] - selv[0]);
+    float myv = 0.f;
+    int myi = 0;
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_K; ++k)
+        if (k == lane) {
+            myv = selv[k];
+            myi = seli[k];
+        }
+    if (lane < K) {
+        ids[lane] = myi;
+        w[lane] = expf(myv - selv[0]) / s;
+    }
+}
+
+}  // namespace moe

@@ -4,7 +4,7 @@
 // v3 artifact", table "What is inside": the router and router scale are FP32.
 // Each token keeps the K largest logits (descending; equal logits in ascending
 // expert order) with softmax weights over the K kept logits.
-#include "kernels.h"
+#include "route_dev.h"
 
 namespace moe {
 
@@ -129,71 +129,92 @@ __global__ __launch_bounds__(256) void router_logits_tiled(const void* __restric
     }
 }
 
-// ---------------------------------------------------------------------------
-// Top-K: one wave per token; lane l holds the logits of experts l, l+64, l+128,
-// l+192.  Each of the K rounds takes the wave maximum (DPP) of the untaken
-// logits and the lowest expert index holding it (ballots), so equal logits
-// go in ascending expert order.
+// --------------------------------------------------------------------------// Top-K: one wave per token.
 __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ logits, int64_t T,
                                                     int E, int K, int32_t* __restrict__ ids,
                                                     float* __restrict__ w) {
-    const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    const float* l = logits + t * E;
-    float v[4];
+    topk_token(logits + t * E, E, K, ids + t * K, w + t * K);
+}
+
+
+
+// Few tokens, routing fused into one kernel: the router GEMV by every
+// workgroup (one wave per expert), then the last workgroup to finish (counted
+// with an agent-scope atomic in the workspace) runs top-K for every token and
+// the permutation of the T*K slots, and resets the counter to zero.
+template <int XDT>
+__global__ __launch_bounds__(256) void route_small(const void* __restrict__ x, int T, int H,
+                                                   const float* __restrict__ W,
+                                                   const float* __restrict__ rsc,
+                                                   const float* __restrict__ bias, int E, int K,
+                                                   float* __restrict__ logits,
+                                                   int32_t* __restrict__ ids, float* __restrict__ w,
+                                                   int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ sorted_slots,
+                                                   int32_t* __restrict__ slot_pos,
+                                                   int* __restrict__ counter) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = blockIdx.x * 4 + wave;
+    if (e < E) {
+        const float* wr = W + (int64_t)e * H;
+        const int H4 = H >> 2;
+        float4 wv[ROUTER_MAX_CHUNKS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = e < E ? l[e] + 0.f : -INFINITY;  // + 0 turns -0 into +0
-    }
-    bool live[4];
+        for (int c = 0; c < ROUTER_MAX_CHUNKS; ++c) {
+            wv[c] = reinterpret_cast<const float4*>(wr)[min(lane + 64 * c, H4 - 1)];
+            if (lane + 64 * c >= H4) wv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        if (rsc) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) live[i] = lane + 64 * i < E;
-    float selv[MOE_MAX_K];
-    int seli[MOE_MAX_K];
-#pragma unroll
-    for (int k = 0; k < MOE_MAX_K; ++k) {
-        selv[k] = 0.f;
-        seli[k] = 0;
-        if (k < K) {
-            float m = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (live[i]) m = fmaxf(m, v[i]);
-            m = wave_max(m);
-            int idx = -1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint64_t bal = __ballot(live[i] && v[i] == m);
-                if (idx < 0 && bal) idx = 64 * i + (int)__builtin_ctzll(bal);
-            }
-            if (idx < 0) idx = 0;  // only when every remaining logit is NaN
-            selv[k] = m;
-            seli[k] = idx;
-            if ((idx & 63) == lane) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (i == (idx >> 6)) live[i] = false;
+            for (int c = 0; c < ROUTER_MAX_CHUNKS; ++c) {
+                const float4 sv = reinterpret_cast<const float4*>(rsc)[min(lane + 64 * c, H4 - 1)];
+                wv[c].x *= sv.x; wv[c].y *= sv.y; wv[c].z *= sv.z; wv[c].w *= sv.w;
             }
         }
-    }
-    float s = 0.f;
+        const float b = bias ? bias[e] : 0.f;
+        for (int t = 0; t < T; ++t) {
+            float acc = 0.f;
 #pragma unroll
-    for (int k = 0; k < MOE_MAX_K; ++k)
-        if (k < K) s += expf(selv[k] - selv[0]);
-    float myv = 0.f;
-    int myi = 0;
-#pragma unroll
-    for (int k = 0; k < MOE_MAX_K; ++k)
-        if (k == lane) {
-            myv = selv[k];
-            myi = seli[k];
+            for (int c = 0; c < ROUTER_MAX_CHUNKS; ++c) {
+                const float4 xv = load_x4(x, XDT, (int64_t)t * H4 + min(lane + 64 * c, H4 - 1));
+                acc = fmaf(xv.x, wv[c].x, acc);
+                acc = fmaf(xv.y, wv[c].y, acc);
+                acc = fmaf(xv.z, wv[c].z, acc);
+                acc = fmaf(xv.w, wv[c].w, acc);
+            }
+            const float s = wave_sum(acc);
+            if (lane == 0) logits[(int64_t)t * E + e] = s + b;
         }
-    if (lane < K) {
-        ids[t * K + lane] = myi;
-        w[t * K + lane] = expf(myv - selv[0]) / s;
     }
+    __shared__ int s_last;
+    __syncthreads();  // this workgroup's logits are written
+    if (threadIdx.x == 0) {
+        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (old == (int)gridDim.x - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every workgroup's logits are visible
+    for (int t = wave; t < T; t += 4) topk_token(logits + (int64_t)t * E, E, K, ids + t * K, w + t * K);
+    __syncthreads();  // ids of every token are written
+    permute_block(ids, T * K, E, offsets, sorted_slots, slot_pos);
+    if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_route_small(const void* x, int x_dt, int T, int H, const float* W,
+                              const float* rsc, const float* bias, int E, int K, float* logits,
+                              int32_t* ids, float* w, int32_t* offsets, int32_t* sorted_slots,
+                              int32_t* slot_pos, int* counter, hipStream_t st) {
+    dim3 grid((E + 3) / 4);
+    if (x_dt == MOE_F32)
+        route_small<MOE_F32><<<grid, 256, 0, st>>>(x, T, H, W, rsc, bias, E, K, logits, ids, w,
+                                                   offsets, sorted_slots, slot_pos, counter);
+    else
+        route_small<MOE_BF16><<<grid, 256, 0, st>>>(x, T, H, W, rsc, bias, E, K, logits, ids, w,
+                                                    offsets, sorted_slots, slot_pos, counter);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

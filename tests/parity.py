@@ -27,7 +27,7 @@ def to_dev(a: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
-def run_gpu_layer(L, logits_in=None, bufs=None):
+def run_gpu_layer(L, logits_in=None, bufs=None, fused_route=False):
     """Run the four C-ABI calls on the layer inputs; returns (numpy dict, bufs)."""
     from sparse_moe_amd import binding
     x = to_dev(L.x)
@@ -38,7 +38,7 @@ def run_gpu_layer(L, logits_in=None, bufs=None):
     bias = None if L.router_bias is None else to_dev(L.router_bias)
     li = None if logits_in is None else to_dev(logits_in)
     bufs = binding.moe_layer(x, wr, gu, dn, L.spec.K, expert_scale=sc, logit_bias=bias,
-                             logits_in=li, bufs=bufs)
+                             logits_in=li, bufs=bufs, fused_route=fused_route)
     torch.cuda.synchronize()
     return {k: getattr(bufs, k).cpu().numpy() for k in
             ("logits", "topk_ids", "topk_w", "offsets", "sorted_slots", "slot_pos", "y_sorted",

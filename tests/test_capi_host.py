@@ -75,6 +75,20 @@ def test_permute_validation_and_workspace():
     assert f(A, 2 ** 30, 8, 128, A, A, A, A, 1 << 40, None) == SHAPE   # T*K >= 2^31
 
 
+def test_route_validation_and_workspace():
+    f = lib.moe_route
+    assert lib.moe_route_workspace_bytes(1, 8, 128) == 256
+    assert lib.moe_route_workspace_bytes(4096, 8, 128) == 256 + lib.moe_permute_workspace_bytes(4096, 8, 128)
+    # (x, x_dt, T, H, W_r, r_scale, bias, E, K, logits, ids, w, offsets, sorted, pos, ws, ws_bytes, stream)
+    assert f(A, 0, 1, 2816, A, None, None, 128, 8, A, A, A, A, A, A, A, 16, None) == WS
+    assert f(A, 0, 1, 2816, A, None, None, 128, 8, A, A, A, A, A, A, None, 256, None) == WS
+    assert f(A, 0, 1, 2816, A, None, None, 128, 8, A, A, A, None, A, A, A, 256, None) == NULL
+    assert f(A, 0, 1, 2816, A, None, None, 128, 8, A, A, A, A, MIS, A, A, 256, None) == ALIGN
+    assert f(A, 0, 1, 2816, A, None, None, 128, 0, A, A, A, A, A, A, A, 256, None) == SHAPE
+    assert f(None, 0, 0, 2816, None, None, None, 128, 8, None, None, None, None, None, None, None,
+             0, None) == OK
+
+
 def test_ffn_validation_and_workspace():
     f = lib.moe_expert_ffn_q4_0
     ws = lib.moe_expert_ffn_q4_0_workspace_bytes(4096, 8, 2816, 704, 128, 1)

@@ -18,26 +18,29 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def _run(L, logits_in=None, token_sample=None):
-    print("case: %s T=%d H=%d E=%d K=%d I=%d act=%s" % (L.spec.name, L.x.shape[0], L.spec.H,
-                                                        L.spec.E, L.spec.K, L.spec.I, L.spec.act),
-          flush=True)
-    g, bufs = parity.run_gpu_layer(L, logits_in)
+def _run(L, logits_in=None, token_sample=None, fused_route=False):
+    print("case: %s T=%d H=%d E=%d K=%d I=%d act=%s fused_route=%s" % (
+        L.spec.name, L.x.shape[0], L.spec.H, L.spec.E, L.spec.K, L.spec.I, L.spec.act, fused_route),
+        flush=True)
+    g, bufs = parity.run_gpu_layer(L, logits_in, fused_route=fused_route)
     res = parity.check_layer(L, g, logits_in=logits_in, token_sample=token_sample)
     print("  ->", res, flush=True)
     return g, res
 
 
-def test_tiny_layer():
-    _run(synth.make_layer(synth.SPECS[0]))
+@pytest.mark.parametrize("fused", [False, True])
+def test_tiny_layer(fused):
+    _run(synth.make_layer(synth.SPECS[0]), fused_route=fused)
 
 
-def test_decode_1_token():
-    _run(synth.make_layer(synth.SPECS[1]))
+@pytest.mark.parametrize("fused", [False, True])
+def test_decode_1_token(fused):
+    _run(synth.make_layer(synth.SPECS[1]), fused_route=fused)
 
 
-def test_decode_8_tokens():
-    g, res = _run(synth.make_layer(synth.SPECS[2]))
+@pytest.mark.parametrize("fused", [False, True])
+def test_decode_8_tokens(fused):
+    g, res = _run(synth.make_layer(synth.SPECS[2]), fused_route=fused)
     assert 30 <= res["distinct_experts"] <= 64
 
 
@@ -64,7 +67,20 @@ def test_shape_sweep(T, E, K):
                               "name": "sweep-T%d-E%d-K%d" % (T, E, K)})
     L = synth.make_layer(spec, seed=100 + T)
     sample = None if (E == 8 or T <= 8) else np.arange(0, T, max(1, T // 6))
-    _run(L, token_sample=sample)
+    _run(L, token_sample=sample, fused_route=(T <= 8))
+
+
+def test_fused_route_repeated_calls_reset_the_counter():
+    # the fused routing kernel leaves its completion counter at zero: many calls in a
+    # row on one workspace keep giving the oracle's routing
+    from sparse_moe_amd import binding
+    spec = synth.SPECS[2]
+    bufs = None
+    for seed in range(5):
+        L = synth.make_layer(spec, seed=50 + seed)
+        g, bufs = parity.run_gpu_layer(L, bufs=bufs, fused_route=True)
+        parity.check_layer(L, g)
+    assert int(bufs.ws_route[:4].view(torch.int32).item()) == 0
 
 
 def test_odd_block_count_rows():
