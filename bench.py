@@ -97,10 +97,8 @@ def main():
     def step(i, ev_a=None, ev_b=None):
         s = sets[i % nsets]
         x = xpool[i % npool]
-        binding.moe_router_topk(x, s["wr"], bufs.logits, bufs.topk_ids, bufs.topk_w,
-                                logit_bias=s["bias"])
-        binding.moe_permute(bufs.topk_ids, E, bufs.offsets, bufs.sorted_slots, bufs.slot_pos,
-                            bufs.ws_perm)
+        binding.moe_route(x, s["wr"], bufs.logits, bufs.topk_ids, bufs.topk_w, bufs.offsets,
+                          bufs.sorted_slots, bufs.slot_pos, bufs.ws_route, logit_bias=s["bias"])
         if ev_a is not None:
             ev_a.record()
         binding.moe_expert_ffn_q4_0(x, s["gu"], s["dn"], K, bufs.offsets, bufs.sorted_slots,
@@ -190,7 +188,7 @@ def main():
                    "distinct_experts_per_step": d_avg,
                    "layer_hbm_gbs": layer_hbm, "layer_hbm_frac": layer_hbm / HBM_PEAK_GBS,
                    "wall_s": wall, "timing": "K steps replayed from one HIP graph per weight set"},
-        "roofline": {"kernel": "moe_expert_ffn_q4_0 (gate/up + down Q4_0 GEMV)",
+        "roofline": {"kernel": "moe_expert_ffn_q4_0 (gate/up then down Q4_0 GEMV launches)",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "bytes_per_launch": ffn_bytes, "avg_launch_us": ffn_avg_ms * 1e3},

@@ -146,6 +146,7 @@ moe_status moe_route(const void* x, int x_dt, int64_t T, int32_t H, const float*
  *              for the expert that owns position p
  *   ws         device workspace of at least
  *              moe_expert_ffn_q4_0_workspace_bytes(T, K, H, I, E, x_dt) bytes
+ *              (holds the hidden h); contents need no initialisation
  * Per slot: g = Wg x, u = Wu x, h = GELU_tanh(g) * u rounded to x_dt (the
  * hidden is materialised in the activation type), y = Wd h; GELU_tanh(z) =
  * z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).  Accumulation is fp32 or exact

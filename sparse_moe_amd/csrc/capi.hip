@@ -7,7 +7,6 @@ namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool dtype_ok(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
-size_t act_size(int dt) { return dt == MOE_F32 ? 4 : 2; }
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
@@ -134,7 +133,7 @@ size_t moe_expert_ffn_q4_0_workspace_bytes(int64_t T, int32_t K, int32_t H, int3
         check_dim(I, MOE_MAX_I) != MOE_OK || !dtype_ok(x_dt))
         return 0;
     // hidden h [T*K, I] in the activation dtype
-    return round_up((size_t)(T * K) * (size_t)I * act_size(x_dt), 256);
+    return round_up((size_t)(T * K) * (size_t)I * (x_dt == MOE_F32 ? 4 : 2), 256);
 }
 
 moe_status moe_expert_ffn_q4_0(const void* x, int x_dt, int64_t T, int32_t H,

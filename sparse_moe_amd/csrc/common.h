@@ -38,6 +38,21 @@ MOE_DEV float f16_bits_to_f32(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
 }
 
+// ---- device-coherent accesses ------------------------------------------------------
+// Data passed between workgroups of one launch goes through agent-scope relaxed
+// atomic stores and loads, which are coherent across the chip's L2 slices
+// without the full-cache writeback or invalidate that an agent-scope release or
+// acquire fence costs.  A producer drains its stores (vmcnt(0)) before the
+// relaxed counter update that publishes them; a consumer reads them only after
+// it has seen that update.
+MOE_DEV void coherent_store(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+MOE_DEV float coherent_load(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+MOE_DEV void drain_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
 // ---- GELU with the tanh approximation ----------------------------------------
 // 0.5 z (1 + tanh(a)) = z / (1 + exp(-2a)), a = sqrt(2/pi) (z + 0.044715 z^3);
 // exp through the hardware exp2.

@@ -156,6 +156,12 @@ MOE_DEV void store_span(uint8_t* lds_wave, int lane, const u32x4a4 (&v)[NCH]) {
         *reinterpret_cast<uint4*>(lds_wave + 1024 * i + 16 * lane) = make_uint4(v[i].x, v[i].y, v[i].z, v[i].w);
 }
 
+// steps per wave: gate/up waves cover 2 output rows (row pairs), down waves 8
+template <int MODE, int LPR>
+constexpr int steps_per_wave() {
+    return (MODE == 0) ? ((64 / LPR) >= 2 ? 1 : 2 / (64 / LPR)) : ((64 / LPR) >= 8 ? 1 : 8 / (64 / LPR));
+}
+
 // ---- kernel --------------------------------------------------------------------
 // MODE 0: gate/up rows of the [gate; up] parent -> h = GELU_tanh(g) * u (act dtype)
 // MODE 1: down rows -> y (fp32)
@@ -164,21 +170,21 @@ MOE_DEV void store_span(uint8_t* lds_wave, int lane, const u32x4a4 (&v)[NCH]) {
 // own LDS region with coalesced loads, then lane (g, q) of a step computes block
 // pair q of row g from LDS.  Tokens of the expert are processed in chunks of TC
 // whose activation digits are staged in LDS once per workgroup.
+// One workgroup tile: rows [bx * 4 * RPW, ...) of the by-th active expert.
 template <int MODE, int ADT, int LPR, int TC, int UPW, bool EVEN_NB>
-__global__ __launch_bounds__(256) void ffn_gemv_q4_0(
-    const uint8_t* __restrict__ W, int nb, int I, int H, const void* __restrict__ act,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slots, int K, int E,
-    void* __restrict__ out, int wave_lds_bytes) {
+MOE_DEV void gemv_tile(const uint8_t* __restrict__ W, int nb, int I, int H,
+                       const void* __restrict__ act, const int32_t* __restrict__ offsets,
+                       const int32_t* __restrict__ sorted_slots, int K, int E,
+                       void* __restrict__ out, int wave_lds_bytes, uint8_t* smem, int bx, int by) {
     constexpr int RPS = 64 / LPR;
     constexpr int RPW = RPS * UPW;           // rows (MODE 0: row pairs) per wave
     constexpr int NR = (MODE == 0) ? 2 : 1;  // spans per wave (gate, up)
     // staging loads per span: rows hold at most 2*LPR blocks (36*LPR bytes)
     constexpr int NCH = (RPW * 36 * LPR + 15 + 1023) / 1024;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int s_e, s_p0, s_n, s_wcnt[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    // -- which expert: the blockIdx.y-th expert with at least one slot
+    // -- which expert: the by-th expert with at least one slot
     {
         const int e = tid;
         int o0 = 0, o1 = 0;
@@ -193,7 +199,7 @@ __global__ __launch_bounds__(256) void ffn_gemv_q4_0(
         __syncthreads();
         int before = __popcll(b & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
         for (int w = 0; w < wave; ++w) before += s_wcnt[w];
-        if (ne && before == (int)blockIdx.y) {
+        if (ne && before == by) {
             s_e = e;
             s_p0 = o0;
             s_n = o1 - o0;
@@ -210,7 +216,7 @@ __global__ __launch_bounds__(256) void ffn_gemv_q4_0(
     const uint8_t* We = W + (int64_t)e * rows_tot * row_bytes;
     const int g = lane / LPR, q = lane % LPR;
     const int nblk_here = min(2, max(0, nb - 2 * q));
-    const int row0 = (blockIdx.x * 4 + wave) * RPW;      // first output row of this wave
+    const int row0 = (bx * 4 + wave) * RPW;              // first output row of this wave
     const int nrows = max(0, min(RPW, rows_out - row0));
 
     uint8_t* wl = smem + wave * wave_lds_bytes;
@@ -359,8 +365,7 @@ __global__ __launch_bounds__(256) void ffn_gemv_q4_0(
                         const int64_t p = p0 + c0 + t;
                         const int row = row0 + lr;
                         if (MODE == 0)
-                            store_act(out, ADT, p * I + row,
-                                      gelu_tanh(res[u][t][0]) * res[u][t][NR - 1]);
+                            store_act(out, ADT, p * I + row, gelu_tanh(res[u][t][0]) * res[u][t][NR - 1]);
                         else
                             reinterpret_cast<float*>(out)[p * H + row] = res[u][t][0];
                     }
@@ -378,13 +383,23 @@ __global__ __launch_bounds__(256) void ffn_gemv_q4_0(
     }
 }
 
+template <int MODE, int ADT, int LPR, int TC, int UPW, bool EVEN_NB>
+__global__ __launch_bounds__(256) void ffn_gemv_q4_0(
+    const uint8_t* __restrict__ W, int nb, int I, int H, const void* __restrict__ act,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slots, int K, int E,
+    void* __restrict__ out, int wave_lds_bytes) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    gemv_tile<MODE, ADT, LPR, TC, UPW, EVEN_NB>(W, nb, I, H, act, offsets, sorted_slots, K, E, out,
+                                                wave_lds_bytes, smem, blockIdx.x, blockIdx.y);
+}
+
 // ---- dispatch ---------------------------------------------------------------------
 template <int MODE, int ADT, int LPR, int TC, bool EVEN_NB>
 static void launch_mode(const uint8_t* W, int nb, int I, int H, const void* act,
                         const int32_t* offsets, const int32_t* sorted_slots, int K, int E,
                         int n_active, void* out, hipStream_t st) {
     constexpr int RPS = 64 / LPR;
-    constexpr int UPW = (MODE == 0) ? (RPS >= 2 ? 1 : 2 / RPS) : (RPS >= 8 ? 1 : 8 / RPS);
+    constexpr int UPW = steps_per_wave<MODE, LPR>();
     constexpr int RPW = RPS * UPW;
     constexpr int NR = (MODE == 0) ? 2 : 1;
     const int rows_out = (MODE == 0) ? I : H;

@@ -7,7 +7,9 @@ namespace moe {
 
 constexpr int ROUTER_GEMV_MAX_T = 8;   // router: per-expert GEMV up to this many tokens
 constexpr int PERM_TILE = 1024;        // permutation: slots per tile (256 threads x 4)
-constexpr int DIGIT_NMAX = 30583;      // largest |n| with 4 balanced base-16 digits: 7*(1+16+256+4096)
+constexpr int DIGIT_NMAX = 30583;
+constexpr int FUSED_FFN_MAX_T = 16;    // expert FFN: gate/up + down in one launch up to this many tokens
+constexpr int FFN_CTL_BYTES = 4 * (4 + MOE_MAX_E);  // counters of the fused launch      // largest |n| with 4 balanced base-16 digits: 7*(1+16+256+4096)
 
 hipError_t launch_router_logits(const void* x, int x_dt, int64_t T, int H, const float* W,
                                 const float* rsc, const float* bias, int E, float* logits,

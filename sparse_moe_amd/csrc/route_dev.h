@@ -60,8 +60,10 @@ MOE_DEV void permute_block(const int32_t* ids, int N, int E, int32_t* offsets,
     const int tid = threadIdx.x, wave = tid >> 6;
     run[tid] = 0;  // blockDim == MOE_MAX_E
     int rank[PERM_TILE / 256], ex[PERM_TILE / 256];
+    const int rounds = (N + 255) / 256;  // <= PERM_TILE / 256
 #pragma unroll
     for (int r = 0; r < PERM_TILE / 256; ++r) {
+        if (r >= rounds) break;
         const int s = r * 256 + tid;
         const bool valid = s < N;
         const int e = valid ? ids[s] : 0;
@@ -87,6 +89,7 @@ MOE_DEV void permute_block(const int32_t* ids, int N, int E, int32_t* offsets,
     block_exclusive_scan256(run, E, tmp, offsets, off);
 #pragma unroll
     for (int r = 0; r < PERM_TILE / 256; ++r) {
+        if (r >= rounds) break;
         const int s = r * 256 + tid;
         if (ex[r] >= 0) {
             const int pos = off[ex[r]] + rank[r];
@@ -101,6 +104,8 @@ MOE_DEV void permute_block(const int32_t* ids, int N, int E, int32_t* offsets,
 // untaken logits and the lowest expert index holding it (ballots), so equal
 // logits go in ascending expert order.  Weights: softmax over the K kept
 // logits.  Every lane of the wave must be active.
+// COH: the logits were written by other workgroups of this launch (coherent loads).
+template <bool COH = false>
 MOE_DEV void topk_token(const float* l, int E, int K, int32_t* ids, float* w) {
     const int lane = threadIdx.x & 63;
     float v[4];
@@ -109,7 +114,8 @@ MOE_DEV void topk_token(const float* l, int E, int K, int32_t* ids, float* w) {
     for (int i = 0; i < 4; ++i) {
         const int e = lane + 64 * i;
         live[i] = e < E;
-        v[i] = live[i] ? l[e] + 0.f : -INFINITY;  // + 0 turns -0 into +0
+        const float le = live[i] ? (COH ? coherent_load(l + e) : l[e]) : 0.f;
+        v[i] = live[i] ? le + 0.f : -INFINITY;  // + 0 turns -0 into +0
     }
     float selv[MOE_MAX_K];
     int seli[MOE_MAX_K];

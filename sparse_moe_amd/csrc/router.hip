@@ -141,9 +141,10 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ lo
 
 
 // Few tokens, routing fused into one kernel: the router GEMV by every
-// workgroup (one wave per expert), then the last workgroup to finish (counted
-// with an agent-scope atomic in the workspace) runs top-K for every token and
-// the permutation of the T*K slots, and resets the counter to zero.
+// workgroup (one wave per expert, logits written with coherent stores), then
+// the last workgroup to finish (counted with an agent-scope atomic in the
+// workspace) runs top-K for every token on coherently loaded logits and the
+// permutation of the T*K slots, and resets the counter to zero.
 template <int XDT>
 __global__ __launch_bounds__(256) void route_small(const void* __restrict__ x, int T, int H,
                                                    const float* __restrict__ W,
@@ -185,19 +186,20 @@ __global__ __launch_bounds__(256) void route_small(const void* __restrict__ x, i
                 acc = fmaf(xv.w, wv[c].w, acc);
             }
             const float s = wave_sum(acc);
-            if (lane == 0) logits[(int64_t)t * E + e] = s + b;
+            if (lane == 0) coherent_store(logits + (int64_t)t * E + e, s + b);
         }
     }
     __shared__ int s_last;
-    __syncthreads();  // this workgroup's logits are written
+    drain_stores();
+    __syncthreads();  // this workgroup's logits are complete
     if (threadIdx.x == 0) {
-        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old == (int)gridDim.x - 1);
     }
     __syncthreads();
     if (!s_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every workgroup's logits are visible
-    for (int t = wave; t < T; t += 4) topk_token(logits + (int64_t)t * E, E, K, ids + t * K, w + t * K);
+    for (int t = wave; t < T; t += 4)
+        topk_token<true>(logits + (int64_t)t * E, E, K, ids + t * K, w + t * K);
     __syncthreads();  // ids of every token are written
     permute_block(ids, T * K, E, offsets, sorted_slots, slot_pos);
     if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
