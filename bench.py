@@ -167,6 +167,24 @@ def main():
     ffn_bytes = (d_avg * expert_bytes + T * H * asz + N * I * asz * 2 + N * H * 4)
     achieved = ffn_bytes / (ffn_avg_ms * 1e-3) / 1e9
     layer_hbm = (d_avg * expert_bytes + E * H * 4 + T * H * asz + E * 4 + T * H * 4) / (ms_step * 1e-3) / 1e9
+    # algorithmic FLOPs of the expert FFN: per slot 2 * (2I * H) + 2 * (H * I)
+    ffn_flops = N * 6.0 * H * I
+    mfma_path = spec.act == "bf16" and T >= 64
+    if mfma_path:
+        roofline = {"kernel": "moe_expert_ffn_q4_0 (activation prep, gate/up and down bf16 MFMA "
+                              "grouped GEMM launches)",
+                    "bound": "mfma", "achieved": ffn_flops / (ffn_avg_ms * 1e-3) / 1e12,
+                    "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": ffn_flops / (ffn_avg_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                    "traffic": None, "flops_per_launch": ffn_flops, "avg_launch_us": ffn_avg_ms * 1e3}
+        dtype = "q4_0 x bf16 (exact bf16 MFMA products, fp32 accumulate)"
+    else:
+        roofline = {"kernel": "moe_expert_ffn_q4_0 (gate/up then down Q4_0 GEMV launches)",
+                    "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                    "bytes_per_launch": ffn_bytes, "avg_launch_us": ffn_avg_ms * 1e3}
+        dtype = "q4_0 x %s (int4 digit products, fp32 accumulate)" % spec.act
+    layer_tflops = ffn_flops / (ms_step * 1e-3) / 1e12
 
     res = {
         "metric": METRIC,
@@ -179,7 +197,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "q4_0 x %s (int4 digit products, fp32 accumulate)" % spec.act,
+        "dtype": dtype,
         "data": "synthetic (seeded; random-init Q4_0 experts, %d weight sets rotated)" % nsets,
         "config": {"workload": "%s: Gemma-4-26B-A4B-shaped routed-MoE layer, T=%d, H=%d, E=%d, "
                                "top-%d, I=%d, Q4_0 experts, %s activations"
@@ -187,11 +205,10 @@ def main():
                    "tokens_per_step": T, "weight_sets": nsets,
                    "distinct_experts_per_step": d_avg,
                    "layer_hbm_gbs": layer_hbm, "layer_hbm_frac": layer_hbm / HBM_PEAK_GBS,
+                   "layer_expert_tflops": layer_tflops,
+                   "layer_mfma_frac": layer_tflops / BF16_PEAK_TFLOPS,
                    "wall_s": wall, "timing": "K steps replayed from one HIP graph per weight set"},
-        "roofline": {"kernel": "moe_expert_ffn_q4_0 (gate/up then down Q4_0 GEMV launches)",
-                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "bytes_per_launch": ffn_bytes, "avg_launch_us": ffn_avg_ms * 1e3},
+        "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(spec, args.cpu_seconds)

@@ -23,6 +23,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the per-block scale FMAs read them
+    # directly instead of through v_accvgpr_read copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

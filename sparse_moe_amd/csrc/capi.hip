@@ -1,6 +1,8 @@
 // C ABI of the routed-MoE library: argument validation, workspace layout and
 // dispatch to the gfx950 kernels.  Nothing here allocates, frees or
 // synchronises; every call only enqueues on the caller's stream.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace {
@@ -132,8 +134,13 @@ size_t moe_expert_ffn_q4_0_workspace_bytes(int64_t T, int32_t K, int32_t H, int3
     if (check_ekh(T, K, E) != MOE_OK || check_dim(H, MOE_MAX_H) != MOE_OK ||
         check_dim(I, MOE_MAX_I) != MOE_OK || !dtype_ok(x_dt))
         return 0;
-    // hidden h [T*K, I] in the activation dtype
-    return round_up((size_t)(T * K) * (size_t)I * (x_dt == MOE_F32 ? 4 : 2), 256);
+    // GEMV path: hidden h [T*K, I] in the activation dtype.  MFMA path (bf16
+    // activations, many tokens): activations and hidden in the MFMA block
+    // order with their block sums.
+    const size_t gemv = round_up((size_t)(T * K) * (size_t)I * (x_dt == MOE_F32 ? 4 : 2), 256);
+    if (x_dt == MOE_BF16 && T >= moe::FFN_MFMA_MIN_T)
+        return std::max(gemv, moe::ffn_mfma_ws_bytes(T, H, I, T * K));
+    return gemv;
 }
 
 moe_status moe_expert_ffn_q4_0(const void* x, int x_dt, int64_t T, int32_t H,
@@ -154,6 +161,11 @@ moe_status moe_expert_ffn_q4_0(const void* x, int x_dt, int64_t T, int32_t H,
     const size_t need = moe_expert_ffn_q4_0_workspace_bytes(T, K, H, I, E, x_dt);
     if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
     if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    if (x_dt == MOE_BF16 && T >= moe::FFN_MFMA_MIN_T)
+        return hip_status(moe::launch_ffn_mfma(x, T, H, (const uint8_t*)w_gate_up,
+                                               (const uint8_t*)w_down, I, E, K, (int)(T * K),
+                                               expert_offsets, sorted_slots, ws, y_sorted,
+                                               (hipStream_t)stream));
     return hip_status(moe::launch_ffn_gemv(x, x_dt, T, H, (const uint8_t*)w_gate_up,
                                            (const uint8_t*)w_down, I, E, K, (int)(T * K),
                                            expert_offsets, sorted_slots, ws, y_sorted,

@@ -53,6 +53,17 @@ MOE_DEV float coherent_load(const float* p) {
 }
 MOE_DEV void drain_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// ---- workgroup barrier ordering LDS only ------------------------------------------
+// __syncthreads() fences all memory, which makes the compiler drain every
+// outstanding global load (vmcnt(0)) at each barrier and defeats prefetching
+// into registers.  Staged LDS tiles only need LDS ordering: a workgroup-scope
+// fence on the local address space waits for LDS (lgkmcnt) alone.
+MOE_DEV void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---- GELU with the tanh approximation ----------------------------------------
 // 0.5 z (1 + tanh(a)) = z / (1 + exp(-2a)), a = sqrt(2/pi) (z + 0.044715 z^3);
 // exp through the hardware exp2.

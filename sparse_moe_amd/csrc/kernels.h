@@ -7,9 +7,8 @@ namespace moe {
 
 constexpr int ROUTER_GEMV_MAX_T = 8;   // router: per-expert GEMV up to this many tokens
 constexpr int PERM_TILE = 1024;        // permutation: slots per tile (256 threads x 4)
-constexpr int DIGIT_NMAX = 30583;
-constexpr int FUSED_FFN_MAX_T = 16;    // expert FFN: gate/up + down in one launch up to this many tokens
-constexpr int FFN_CTL_BYTES = 4 * (4 + MOE_MAX_E);  // counters of the fused launch      // largest |n| with 4 balanced base-16 digits: 7*(1+16+256+4096)
+constexpr int DIGIT_NMAX = 30583;       // largest |n| with 4 balanced base-16 digits: 7*(1+16+256+4096)
+constexpr int FFN_MFMA_MIN_T = 64;     // expert FFN: bf16 MFMA grouped GEMM from this many tokens
 
 hipError_t launch_router_logits(const void* x, int x_dt, int64_t T, int H, const float* W,
                                 const float* rsc, const float* bias, int E, float* logits,
@@ -28,6 +27,12 @@ hipError_t launch_permute(const int32_t* ids, int N, int E, int32_t* offsets, in
 hipError_t launch_ffn_gemv(const void* x, int x_dt, int64_t T, int H, const uint8_t* w_gate_up,
                            const uint8_t* w_down, int I, int E, int K, int N,
                            const int32_t* offsets, const int32_t* sorted_slots, void* h_ws,
+                           float* y_sorted, hipStream_t st);
+
+size_t ffn_mfma_ws_bytes(int64_t T, int H, int I, int64_t N);
+hipError_t launch_ffn_mfma(const void* x, int64_t T, int H, const uint8_t* w_gate_up,
+                           const uint8_t* w_down, int I, int E, int K, int N,
+                           const int32_t* offsets, const int32_t* sorted_slots, void* ws,
                            float* y_sorted, hipStream_t st);
 
 hipError_t launch_combine(const float* y, const int32_t* slot_pos, const int32_t* ids,

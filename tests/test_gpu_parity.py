@@ -120,3 +120,18 @@ def test_deterministic_and_fully_written():
         outs.append(g)
     for k in outs[0]:
         assert np.array_equal(outs[0][k].view(np.uint8), outs[1][k].view(np.uint8)), k
+
+
+@pytest.mark.parametrize("H,I,E,K,T", [
+    (288, 96, 8, 2, 70),       # odd block counts per row (9 and 3): unaligned Q4_0 rows
+    (256, 64, 8, 2, 600),      # ~150 slots per expert: two slot tiles per expert
+    (256, 96, 4, 1, 300),      # K = 1, a partial second column tile of the gate/up product
+    (2816, 704, 128, 8, 64),   # Gemma shape at the smallest token count of the MFMA path
+])
+def test_mfma_path_shapes(H, I, E, K, T):
+    # bf16 activations with T >= 64 take the bf16 MFMA grouped GEMM
+    spec = synth.LayerSpec("mfma-H%d-I%d-E%d-K%d-T%d" % (H, I, E, K, T), H=H, E=E, K=K, I=I, T=T,
+                           act="bf16", router_std=1 / np.sqrt(H), seed=11)
+    L = synth.make_layer(spec)
+    sample = None if H < 1024 else np.arange(0, T, 5)
+    _run(L, token_sample=sample)
