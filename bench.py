@@ -33,7 +33,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", type=int, default=1, help="workload index (1: decode 1 token)")
+    p.add_argument("--config", type=int, default=1,
+                   help="workload: 0 tiny, 1 decode 1 token, 2 decode 8 tokens, 3 prefill 4096, "
+                        "4 stack of 30 layers x 512 tokens")
     p.add_argument("--sets", type=int, default=0, help="weight sets rotated (0: auto)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -44,6 +46,8 @@ def cpu_baseline(spec, seconds: float):
     """The oracle as it stands, single-threaded, on a bounded token sample."""
     import oracle
     from sparse_moe_amd import synth
+    if spec.layers > 1:
+        return cpu_baseline_stack(spec, seconds)
     L = synth.make_layer(spec, T=1)
     xs = synth.activations(spec, 64, spec.seed + 77)
     n, t0 = 0, time.perf_counter()
@@ -60,6 +64,169 @@ def cpu_baseline(spec, seconds: float):
                       "single-threaded binary64 C oracle" % (n, spec.name, spec.K, spec.K)}
 
 
+def bench_stack(args, spec):
+    """Stack workload: one step = all layers (RMSNorm -> routing -> expert FFN ->
+    combine with residual) over one chunk; every layer has its own weights, all
+    resident (no rotation needed: 30 layers of experts far exceed the caches)."""
+    import torch
+    from sparse_moe_amd import binding, synth
+    T, H, E, K, I = spec.T, spec.H, spec.E, spec.K, spec.I
+    dev = "cuda"
+
+    def dev_t(a):
+        import numpy as np
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    layers = []
+    for l in range(spec.layers):
+        L = synth.make_layer(spec, seed=synth.stack_layer_seed(l), with_x=False)
+        layers.append(dict(wr=dev_t(L.w_router), gu=dev_t(L.w_gate_up), dn=dev_t(L.w_down),
+                           sc=dev_t(L.expert_scale), bias=dev_t(L.router_bias),
+                           rw=dev_t(L.rms_w)))
+        del L
+    x0 = dev_t(synth.activations(spec, T, spec.seed))
+    xa, xb, xhat = x0.clone(), torch.empty_like(x0), torch.empty_like(x0)
+    bufs = [binding.LayerBuffers(T, H, I, E, K, torch.bfloat16) for _ in range(2)]
+
+    def step(evs=None):
+        xin, xout = xa, xb
+        xin.copy_(x0)
+        for l, w in enumerate(layers):
+            b = bufs[l & 1]
+            binding.moe_rmsnorm(xin, w["rw"], spec.rms_eps, xhat)
+            binding.moe_route(xhat, w["wr"], b.logits, b.topk_ids, b.topk_w, b.offsets,
+                              b.sorted_slots, b.slot_pos, b.ws_route, logit_bias=w["bias"])
+            if evs is not None:
+                evs[l][0].record()
+            binding.moe_expert_ffn_q4_0(xhat, w["gu"], w["dn"], K, b.offsets, b.sorted_slots,
+                                        b.y_sorted, b.ws_ffn)
+            if evs is not None:
+                evs[l][1].record()
+            binding.moe_combine(b.y_sorted, b.slot_pos, b.topk_ids, b.topk_w, w["sc"],
+                                residual=xin, out_act=xout, out_f32=b.out)
+            xin, xout = xout, xin
+
+    # distinct experts per layer (for the algorithmic bytes)
+    distinct = []
+    xin, xout = xa, xb
+    xin.copy_(x0)
+    for l, w in enumerate(layers):
+        b = bufs[0]
+        binding.moe_rmsnorm(xin, w["rw"], spec.rms_eps, xhat)
+        binding.moe_route(xhat, w["wr"], b.logits, b.topk_ids, b.topk_w, b.offsets,
+                          b.sorted_slots, b.slot_pos, b.ws_route, logit_bias=w["bias"])
+        binding.moe_expert_ffn_q4_0(xhat, w["gu"], w["dn"], K, b.offsets, b.sorted_slots,
+                                    b.y_sorted, b.ws_ffn)
+        binding.moe_combine(b.y_sorted, b.slot_pos, b.topk_ids, b.topk_w, w["sc"],
+                            residual=xin, out_act=xout, out_f32=b.out)
+        torch.cuda.synchronize()
+        distinct.append(int((b.offsets[1:] - b.offsets[:-1] > 0).sum().item()))
+        xin, xout = xout, xin
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    out_graph = (xa if spec.layers % 2 == 0 else xb).clone()
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(out_graph, xa if spec.layers % 2 == 0 else xb), "graph replay differs"
+
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    t0.record()
+    for _ in range(args.steps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in layers]
+    reps = max(1, min(args.steps, 5))
+    ffn_ms = [0.0] * len(layers)
+    for _ in range(reps):
+        step(evs)
+        torch.cuda.synchronize()
+        for l, (a, b) in enumerate(evs):
+            ffn_ms[l] += a.elapsed_time(b) / reps
+    expert_bytes = Q4_0_EXPERT_BYTES(H, I)
+    N = T * K
+    ffn_flops = N * 6.0 * H * I
+    ffn_total_ms = sum(ffn_ms)
+    ffn_bytes = [d * expert_bytes + T * H * 2 + N * I * 2 * 2 + N * H * 4 for d in distinct]
+    achieved_gbs = sum(ffn_bytes) / (ffn_total_ms * 1e-3) / 1e9
+    achieved_tf = ffn_flops * len(layers) / (ffn_total_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": T * args.steps / (ms_total * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "q4_0 x bf16 (exact bf16 MFMA products, fp32 accumulate)",
+        "data": "synthetic (seeded; random-init Q4_0 experts, one weight set per layer)",
+        "config": {"workload": "%s: %d Gemma-4-26B-A4B-shaped routed-MoE layers with RMSNorm and "
+                               "residual, T=%d, H=%d, E=%d, top-%d, I=%d, Zipf(%.1f) router prior, "
+                               "bf16 activations" % (spec.name, spec.layers, T, H, E, K, I,
+                                                     spec.zipf_s),
+                   "tokens_per_step": T, "layers": spec.layers,
+                   "distinct_experts_per_layer_mean": sum(distinct) / len(distinct),
+                   "distinct_experts_per_layer_min_max": [min(distinct), max(distinct)],
+                   "ffn_mfma_tflops": achieved_tf, "ffn_mfma_frac": achieved_tf / BF16_PEAK_TFLOPS,
+                   "wall_s": wall, "timing": "K steps, each a replay of one HIP graph of all layers"},
+        "roofline": {"kernel": "moe_expert_ffn_q4_0 over the layers (activation prep, gate/up and "
+                               "down bf16 MFMA grouped GEMM launches)",
+                     "bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": sum(ffn_bytes) / len(ffn_bytes),
+                     "avg_launch_us": ffn_total_ms / len(layers) * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(spec, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_stack(spec, seconds: float):
+    """Stack workload: tokens one at a time through the first two layers (RMSNorm,
+    layer, residual), the rate scaled to all layers."""
+    import numpy as np
+    import oracle
+    from sparse_moe_amd import synth
+    Ls = [synth.make_layer(spec, seed=synth.stack_layer_seed(l), T=1, with_x=False) for l in range(2)]
+    xs = synth.activations(spec, 64, spec.seed + 77)
+    n, t0 = 0, time.perf_counter()
+    while n < xs.shape[0]:
+        x = xs[n:n + 1]
+        for L in Ls:
+            xh = oracle.rmsnorm(x, L.rms_w, spec.rms_eps)
+            r = oracle.moe_layer(xh, L.w_router, L.w_gate_up, L.w_down, spec.K,
+                                 scale=L.expert_scale, bias=L.router_bias)
+            xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            x = synth.f32_to_bf16_bits((xf + r["out"]).astype(np.float32))
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    per_token_layer = dt / (n * len(Ls))
+    return {"value": 1.0 / (per_token_layer * spec.layers), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d tokens one at a time through 2 of the %d layers (RMSNorm, router with "
+                      "Zipf prior over all experts, top-%d, %d expert FFNs, combine, residual), "
+                      "single-threaded binary64 C oracle; rate scaled to %d layers"
+                      % (n, spec.layers, spec.K, spec.K, spec.layers)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -70,6 +237,8 @@ def main():
     from sparse_moe_amd import binding, synth
     torch.cuda.set_device(0)
     spec = synth.SPECS[args.config]
+    if spec.layers > 1:
+        return bench_stack(args, spec)
     T, H, E, K, I = spec.T, spec.H, spec.E, spec.K, spec.I
     act = torch.float32 if spec.act == "f32" else torch.bfloat16
     dev = "cuda"
