@@ -138,7 +138,7 @@ size_t moe_expert_ffn_q4_0_workspace_bytes(int64_t T, int32_t K, int32_t H, int3
     // activations, many tokens): activations and hidden in the MFMA block
     // order with their block sums.
     const size_t gemv = round_up((size_t)(T * K) * (size_t)I * (x_dt == MOE_F32 ? 4 : 2), 256);
-    if (x_dt == MOE_BF16 && T >= moe::FFN_MFMA_MIN_T)
+    if (moe::ffn_use_mfma(x_dt, T, H, I))
         return std::max(gemv, moe::ffn_mfma_ws_bytes(T, H, I, T * K));
     return gemv;
 }
@@ -161,7 +161,7 @@ moe_status moe_expert_ffn_q4_0(const void* x, int x_dt, int64_t T, int32_t H,
     const size_t need = moe_expert_ffn_q4_0_workspace_bytes(T, K, H, I, E, x_dt);
     if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
     if (!aligned16(ws)) return MOE_ERR_ALIGN;
-    if (x_dt == MOE_BF16 && T >= moe::FFN_MFMA_MIN_T)
+    if (moe::ffn_use_mfma(x_dt, T, H, I))
         return hip_status(moe::launch_ffn_mfma(x, T, H, (const uint8_t*)w_gate_up,
                                                (const uint8_t*)w_down, I, E, K, (int)(T * K),
                                                expert_offsets, sorted_slots, ws, y_sorted,

@@ -21,11 +21,11 @@
 // order together with the block sums; the gate/up epilogue writes the hidden h
 // (rounded to bf16) the same way, so the down product reads it directly.
 //
-// Tiles: 128 slots x 128 weight rows per workgroup of 4 waves (2 x 2, 64 x 64
-// per wave = 4 x 4 MFMA tiles); two Q4_0 blocks per LDS stage.  For gate/up a
-// tile's 128 rows are 64 gate rows and the 64 up rows of the same hidden
-// columns, and each wave holds gate and up of the same (slot, column) in
-// matching registers, so GELU(g) * u is formed in the epilogue.
+// Tiles: 128 slots x 256 weight rows per workgroup of 4 waves, each wave 128
+// slots x 64 rows (8 x 4 MFMA tiles); two Q4_0 blocks per stage.  For gate/up
+// a wave's 64 rows are 32 gate rows and the 32 up rows of the same hidden
+// columns, so each lane holds gate and up of the same (slot, column) in
+// matching registers and GELU(g) * u is formed in the epilogue.
 #include "kernels.h"
 
 namespace moe {
@@ -33,13 +33,14 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2a4 __attribute__((ext_vector_type(2), aligned(4)));
 
 constexpr int MT = 128;        // slots per tile
-constexpr int NT = 128;        // weight rows per tile
+constexpr int NT = 256;        // weight rows per tile (64 per wave)
 constexpr int ROWB = 80;       // LDS bytes per (row, block): 64 data + 16 pad (no bank conflicts)
-// one LDS slot: A [MT rows][80 B], B [NT rows][80 B], D [NT] scales, C [MT] sums
-constexpr int SLOT_BYTES = MT * ROWB + NT * ROWB + 4 * (NT + MT);
-constexpr int LDS_BYTES = 3 * SLOT_BYTES;
+// one LDS slot (a pair of blocks): activations [2][MT rows][80 B], sums [2][MT]
+constexpr int SLOT_BYTES = 2 * MT * ROWB + 2 * MT * 4;
+constexpr int LDS_BYTES = 2 * SLOT_BYTES;
 
 // Position, inside a 32-element block as the MFMA reads it, of element j.
 // Lane group g holds k slots 8g..8g+7 = elements 4g, 4g+2, 4g+16, 4g+18,
@@ -113,10 +114,23 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int tile, 
 //         block sums.
 // MODE 1: down.     act = permuted h [N][I], csum [N][I/32], W = w_down,
 //         rows_e = ncols = H; writes y_sorted.
+// Requires an even number of blocks per row (H and I multiples of 64), so that
+// every pair of blocks starts on a dword boundary.
 //
-// Pipeline over the K blocks (one Q4_0 block per stage, three LDS slots and
-// three register sets): iteration j stores stage j+1 into LDS, issues the
-// global loads of stage j+3, runs the MFMAs of stage j, and ends on a barrier.
+// Tile: MT slots x NT weight rows; wave w owns weight rows 64w..64w+63 of the
+// tile (4 MFMA row fragments) against all MT slots (8 fragments), 128 fp32
+// accumulators per lane.  Each wave loads and unpacks its own weights straight
+// into registers (no LDS): per block pair and row fragment a lane reads 8 + 4
+// bytes of its row's 36-byte window; the two fp16 scales reach the lanes that
+// need them through ds_bpermute.  Only the activations and their block sums go
+// through LDS, shared by the four waves.
+//
+// Pipeline over block pairs j: iteration j stores the activations of pair j+1
+// (loaded one iteration earlier) into LDS slot (j+1)&1, issues the loads of
+// the activations of pair j+2, runs the MFMAs of pair j, then loads the weights
+// of pair j+1 (one register set: a second set does not fit two waves per SIMD
+// and measured no faster), and ends on an LDS-only barrier.  Loads are unconditional
+// (clamped past the end) so the compiler's wait counts stay exact.
 template <int MODE>
 __global__ __launch_bounds__(256) void ffn_mfma(
     const uint16_t* __restrict__ act, const float* __restrict__ csum, const uint8_t* __restrict__ W,
@@ -137,157 +151,167 @@ __global__ __launch_bounds__(256) void ffn_mfma(
     base = __builtin_amdgcn_readfirstlane(base);
     cnt = __builtin_amdgcn_readfirstlane(cnt);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g = lane >> 4;
-    const int wm = wave & 1, wn = wave >> 1;
-    const size_t rowbytes = (size_t)nb * 18;
-    const int col0 = ntile * (MODE == 0 ? NT / 2 : NT);  // first hidden column / output row
+    const uint32_t rowbytes = (uint32_t)nb * 18u;
+    const uint8_t* We = W + (size_t)e * rows_e * rowbytes;
+    const int npairs = nb >> 1;
 
-    // ---- staging role: tile rows r4 and r4 + 64, 16-byte chunk / qs dword q4 ----
-    const int r4 = tid >> 2, q4 = tid & 3;
-    const uint16_t* a_src[2];
-    const float* c_src[2];
-    size_t w_off[2];  // byte offset of the weight row in W (W is 16-byte aligned)
-    int sslot[2];
+    // ---- this wave's weight rows ----
+    // MODE 0: hidden columns c0 .. c0+31 (rows of gate, then the same rows of up)
+    // MODE 1: output rows c0 .. c0+63
+    const int c0 = MODE == 0 ? ntile * (NT / 2) + 32 * wave : ntile * NT + 64 * wave;
+    int nfa;  // valid row fragments (whole wave for MODE 0)
+    if (MODE == 0)
+        nfa = c0 < ncols ? 4 : 0;
+    else
+        nfa = max(0, min(4, (ncols - c0) >> 4));
+    uint32_t woff[4];  // byte offset (in the expert) of this lane's row, plus its qs group
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int r = r4 + 64 * h;
-        const int p = base + min(r, cnt - 1);
-        const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
-        a_src[h] = act + arow * (int64_t)nb * 32 + 8 * q4;
-        c_src[h] = csum + arow * (int64_t)nb;
-        int wrow;
-        if (MODE == 0) {  // tile rows 0..63 gate, 64..127 up, of hidden columns col0 + (0..63)
-            wrow = min(col0 + r4, ncols - 1) + h * ncols;
-            sslot[h] = (r4 >> 5) * 64 + (((r4 >> 4) & 1) + 2 * h) * 16 + (r4 & 15);
-        } else {
-            wrow = min(col0 + r, rows_e - 1);
-            sslot[h] = r;
-        }
-        w_off[h] = ((size_t)e * rows_e + wrow) * rowbytes;
+    for (int nf = 0; nf < 4; ++nf) {
+        int row;
+        if (MODE == 0)
+            row = min(c0 + (nf & 1) * 16 + l16, ncols - 1) + (nf >> 1) * ncols;
+        else
+            row = min(c0 + nf * 16 + l16, rows_e - 1);
+        woff[nf] = (uint32_t)row * rowbytes + 4u * (uint32_t)g;
     }
 
-    // ---- per-wave extent (uniform) ----
-    const int m_rows = cnt - wm * 64;
-    const int mfa = m_rows <= 0 ? 0 : min(4, (m_rows + 15) >> 4);
-    int nfa;
-    if (MODE == 0)
-        nfa = (col0 + wn * 32 < ncols) ? 4 : 0;
-    else
-        nfa = max(0, min(4, (ncols - (col0 + wn * 64)) >> 4));
-    const bool active = mfa > 0 && nfa > 0;
-
-    f32x4 acc[4][4];
+    // ---- activation staging roles: 16-byte chunk ch of tile rows (tid>>3) + 32i ----
+    const int ch = tid & 7, srow = tid >> 3;
+    uint32_t aoff[4];  // element offset of (row, pair 0, chunk) in act
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+        const int r = srow + 32 * i;
+        const int p = base + min(r, cnt - 1);
+        const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
+        aoff[i] = (uint32_t)(arow * nb * 32) + 8u * (uint32_t)ch;
+    }
+    uint32_t coff;  // block-sum offset of tile row (tid & 127)
+    {
+        const int r = tid & (MT - 1);
+        const int p = base + min(r, cnt - 1);
+        const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
+        coff = (uint32_t)(arow * nb);
+    }
+
+    const int mfa = min(8, (cnt + 15) >> 4);  // valid slot fragments
+    const bool active = nfa > 0;
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int jn = 0; jn < 4; ++jn) acc[i][jn] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    // register stage: 2 activation chunks, 2 qs dword pairs, 2 scales, 2 sums
-    struct Stage {
-        u32x4a4 a[2];
-        uint32_t lo[2], hi[2];
-        uint32_t d[2];
-        float c[2];
-        int sh[2];
+    struct AStage {
+        u32x4a4 a[4];
+        float c0, c1;
     };
-    auto load = [&](Stage& S, int b) {
+    struct BStage {
+        uint32_t lo[4], hi[4], q1[4];
+    };
+    auto load_a = [&](AStage& S, int j) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            S.a[h] = *(const u32x4a4*)(a_src[h] + (int64_t)b * 32);
-            const size_t bo = w_off[h] + (size_t)b * 18;         // block start
-            const size_t qo = bo + 2 + 4 * q4;                       // this lane's qs dword
-            const uint32_t* qw = (const uint32_t*)(W + (qo & ~(size_t)3));
-            S.sh[h] = (int)(qo & 3);
-            S.lo[h] = qw[0];
-            // branch-free (every lane issues the same loads, which keeps the
-            // wait counts exact): a straddling qs dword takes its last two bytes
-            // from a 16-bit load that ends inside the block; otherwise the
-            // 16-bit load rereads the first dword and is ignored
-            S.hi[h] = (uint32_t)*(const uint16_t*)(qw + (S.sh[h] ? 1 : 0));
-            S.d[h] = (uint32_t)*(const uint16_t*)(W + bo);
-            S.c[h] = c_src[h][b];
+        for (int i = 0; i < 4; ++i) S.a[i] = *(const u32x4a4*)(act + aoff[i] + (uint32_t)j * 64u);
+        const float* cp = csum + coff + 2u * (uint32_t)j;
+        S.c0 = cp[0];
+        S.c1 = cp[1];
+    };
+    auto store_a = [&](const AStage& S, int slot) {
+        uint8_t* A_lds = smem + slot * SLOT_BYTES;
+        float* C_lds = (float*)(A_lds + 2 * MT * ROWB);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *(u32x4*)(A_lds + ((ch >> 2) * MT + srow + 32 * i) * ROWB + 16 * (ch & 3)) =
+                (u32x4){S.a[i].x, S.a[i].y, S.a[i].z, S.a[i].w};
+        if (tid < MT) {
+            C_lds[tid] = S.c0;
+            C_lds[MT + tid] = S.c1;
         }
     };
-    auto store = [&](const Stage& S, int slot) {
-        uint8_t* A_lds = smem + slot * SLOT_BYTES;
-        uint8_t* B_lds = A_lds + MT * ROWB;
-        float* D_lds = (float*)(B_lds + NT * ROWB);
-        float* C_lds = D_lds + NT;
+    auto load_b = [&](BStage& S, int j) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int r = r4 + 64 * h;
-            *(u32x4*)(A_lds + r * ROWB + 16 * q4) = (u32x4){S.a[h].x, S.a[h].y, S.a[h].z, S.a[h].w};
-            const uint32_t w = __builtin_amdgcn_alignbyte(S.hi[h], S.lo[h], S.sh[h]);
-            *(u32x4*)(B_lds + sslot[h] * ROWB + 16 * q4) = dq_group(w);
-            if (q4 == 0) {
-                C_lds[r] = S.c[h];
-                const int s = sslot[h];
-                D_lds[(((s >> 6) * 16) + (s & 15)) * 4 + ((s >> 4) & 3)] = f16_bits_to_f32(S.d[h]);
+        for (int nf = 0; nf < 4; ++nf) {
+            const uint8_t* wp = We + woff[nf] + (uint32_t)j * 36u;
+            const u32x2a4 v = *(const u32x2a4*)wp;  // qs0 bytes 4g-2 .. 4g+5 (d0 in lane g=0)
+            S.lo[nf] = v.x;
+            S.hi[nf] = v.y;                          // lane g=3: bytes 16..19, d1 in the top half
+            S.q1[nf] = *(const uint32_t*)(wp + 20);  // qs1 bytes 4g .. 4g+3
+        }
+    };
+    auto compute = [&](int slot, const BStage& S) {
+        const uint8_t* A_lds = smem + slot * SLOT_BYTES;
+        const float* C_lds = (const float*)(A_lds + 2 * MT * ROWB);
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            // this block's weights: unpack the lane's qs dword, fetch the scale of
+            // its row from the lane of group 0 (block 0) or group 3 (block 1)
+            float dv[4];
+            u32x4 bq[4];
+#pragma unroll
+            for (int nf = 0; nf < 4; ++nf) {
+                if (blk == 0) {
+                    const uint32_t d0 = (uint32_t)__shfl((int)S.lo[nf], l16);
+                    dv[nf] = f16_bits_to_f32(d0 & 0xFFFFu);
+                    bq[nf] = dq_group(__builtin_amdgcn_alignbyte(S.hi[nf], S.lo[nf], 2));
+                } else {
+                    const uint32_t d1 = (uint32_t)__shfl((int)S.hi[nf], 48 + l16);
+                    dv[nf] = f16_bits_to_f32(d1 >> 16);
+                    bq[nf] = dq_group(S.q1[nf]);
+                }
+                // keep the scale a plain fp32 register: otherwise the compiler folds
+                // the fp16 conversion into v_fma_mix_f32 for every scale FMA, which
+                // issues slower and raises register pressure into spills
+                asm volatile("" : "+v"(dv[nf]));
+            }
+            // every slot fragment, unconditionally (rows past the count are computed
+            // and dropped at the store): per-fragment branches cost registers and
+            // serialise the schedule
+#pragma unroll
+            for (int mf = 0; mf < 8; ++mf) {
+                const int r = blk * MT + mf * 16;
+                const u32x4 a = *(const u32x4*)(A_lds + (r + l16) * ROWB + 16 * g);
+                const f32x4 c = *(const f32x4*)&C_lds[r + 4 * g];
+                f32x4 t[4];
+#pragma unroll
+                for (int nf = 0; nf < 4; ++nf) t[nf] = mfma_bf16(a, bq[nf], c);
+#pragma unroll
+                for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[mf][nf][i] = fmaf(dv[nf], t[nf][i], acc[mf][nf][i]);
             }
         }
     };
-    auto compute = [&](int slot) {
-        const uint8_t* A_lds = smem + slot * SLOT_BYTES;
-        const uint8_t* B_lds = A_lds + MT * ROWB;
-        const float* D_lds = (const float*)(B_lds + NT * ROWB);
-        const float* C_lds = D_lds + NT;
-        const f32x4 dv = *(const f32x4*)&D_lds[(wn * 16 + l16) * 4];
-        u32x4 bq[4];
-#pragma unroll
-        for (int nf = 0; nf < 4; ++nf)
-            bq[nf] = *(const u32x4*)(B_lds + (wn * 64 + nf * 16 + l16) * ROWB + 16 * g);
-#pragma unroll
-        for (int mf = 0; mf < 4; ++mf) {
-            const int r = wm * 64 + mf * 16;
-            const u32x4 a = *(const u32x4*)(A_lds + (r + l16) * ROWB + 16 * g);
-            const f32x4 c = *(const f32x4*)&C_lds[r + 4 * g];
-            f32x4 t[4];
-#pragma unroll
-            for (int nf = 0; nf < 4; ++nf) t[nf] = mfma_bf16(a, bq[nf], c);
-#pragma unroll
-            for (int nf = 0; nf < 4; ++nf)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[mf][nf][i] = fmaf(dv[nf], t[nf][i], acc[mf][nf][i]);
-        }
-    };
 
-    // stage s lives in register set s % 3 and LDS slot s % 3: its loads are
-    // issued two iterations before the iteration that stores it to LDS
-    Stage R0, R1, R2;
-    load(R0, 0);
-    load(R1, min(1, nb - 1));
-    load(R2, min(2, nb - 1));
-    store(R0, 0);
+    AStage RA;
+    BStage RB;
+    load_a(RA, 0);
+    load_b(RB, 0);
+    store_a(RA, 0);
+    load_a(RA, min(1, npairs - 1));
     lds_barrier();
-    auto iter = [&](int jj, int cs, int ns, const Stage& Rst, Stage& Rld) {
-        if (jj + 1 < nb) store(Rst, ns);
-        // unconditional (clamped past the end) so every path issues the same
-        // loads and the compiler's wait counts stay exact
-        load(Rld, min(jj + 3, nb - 1));
-        if (active) compute(cs);
+    for (int j = 0; j < npairs; ++j) {
+        store_a(RA, (j + 1) & 1);
+        load_a(RA, min(j + 2, npairs - 1));
+        if (active) compute(j & 1, RB);
+        load_b(RB, min(j + 1, npairs - 1));
         lds_barrier();
-    };
-    for (int j = 0; j < nb; j += 3) {
-        iter(j, 0, 1, R1, R0);
-        if (j + 1 >= nb) break;
-        iter(j + 1, 1, 2, R2, R1);
-        if (j + 2 >= nb) break;
-        iter(j + 2, 2, 0, R0, R2);
     }
 
     if (!active) return;
     if (MODE == 0) {
-        // h = GELU(g) * u for hidden columns col0 + wn*32 + (0..31): one Q4_0
-        // block of the down product's K, written in the MFMA order with its sum.
+        // h = GELU(g) * u for hidden columns c0 .. c0+31: one Q4_0 block of the
+        // down product's K, written in the MFMA order with its sum.
         const int I = ncols, nbh = I >> 5;
-        const int hblk = (col0 >> 5) + wn;
+        const int hblk = c0 >> 5;
 #pragma unroll
-        for (int mf = 0; mf < 4; ++mf) {
+        for (int mf = 0; mf < 8; ++mf) {
             if (mf < mfa) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = wm * 64 + mf * 16 + 4 * g + i;
+                    const int r = mf * 16 + 4 * g + i;
                     const bool ok = r < cnt;
                     const int64_t p = base + min(r, cnt - 1);
                     float s = 0.f;
@@ -310,13 +334,13 @@ __global__ __launch_bounds__(256) void ffn_mfma(
     } else {
         const int H = ncols;
 #pragma unroll
-        for (int mf = 0; mf < 4; ++mf) {
+        for (int mf = 0; mf < 8; ++mf) {
             if (mf < mfa) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = wm * 64 + mf * 16 + 4 * g + i;
+                    const int r = mf * 16 + 4 * g + i;
                     if (r < cnt) {
-                        float* yp = y_out + (int64_t)(base + r) * H + col0 + wn * 64 + l16;
+                        float* yp = y_out + (int64_t)(base + r) * H + c0 + l16;
 #pragma unroll
                         for (int nf = 0; nf < 4; ++nf)
                             if (nf < nfa) yp[nf * 16] = 16.f * acc[mf][nf][i];

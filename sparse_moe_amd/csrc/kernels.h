@@ -29,6 +29,11 @@ hipError_t launch_ffn_gemv(const void* x, int x_dt, int64_t T, int H, const uint
                            const int32_t* offsets, const int32_t* sorted_slots, void* h_ws,
                            float* y_sorted, hipStream_t st);
 
+// bf16 activations, enough tokens, and rows of an even number of Q4_0 blocks
+// (every block pair dword aligned)
+inline bool ffn_use_mfma(int x_dt, int64_t T, int H, int I) {
+    return x_dt == MOE_BF16 && T >= FFN_MFMA_MIN_T && H % 64 == 0 && I % 64 == 0;
+}
 size_t ffn_mfma_ws_bytes(int64_t T, int H, int I, int64_t N);
 hipError_t launch_ffn_mfma(const void* x, int64_t T, int H, const uint8_t* w_gate_up,
                            const uint8_t* w_down, int I, int E, int K, int N,

@@ -123,9 +123,9 @@ def test_deterministic_and_fully_written():
 
 
 @pytest.mark.parametrize("H,I,E,K,T", [
-    (288, 96, 8, 2, 70),       # odd block counts per row (9 and 3): unaligned Q4_0 rows
+    (288, 96, 8, 2, 70),       # odd block counts per row (9 and 3): served by the GEMV path
     (256, 64, 8, 2, 600),      # ~150 slots per expert: two slot tiles per expert
-    (256, 96, 4, 1, 300),      # K = 1, a partial second column tile of the gate/up product
+    (256, 192, 4, 1, 300),     # K = 1, a partial second column tile of the gate/up product
     (2816, 704, 128, 8, 64),   # Gemma shape at the smallest token count of the MFMA path
 ])
 def test_mfma_path_shapes(H, I, E, K, T):
