@@ -220,10 +220,153 @@ hipError_t launch_route_small(const void* x, int x_dt, int T, int H, const float
 }
 
 // ---------------------------------------------------------------------------
+
+// ---------------------------------------------------------------------------
+// Many tokens, bf16 activations: logits on bf16 MFMA (v_mfma_f32_16x16x32_bf16).
+// Each fp32 router weight (times the router scale, when given) is split by bit
+// truncation into three bf16 parts hi + mid + lo that add up to it exactly (the
+// top 8, next 8 and last 8 significant bits of fp32's 24), so
+// x W = x hi + x mid + x lo: exact products, fp32 accumulation, three MFMAs per
+// K step.  Workgroup tile: 32 tokens x 32 experts (each weight fragment and its
+// split serve two token fragments); its 4 waves take a quarter of H each and
+// add their partial sums through LDS in a fixed order.
+typedef __attribute__((ext_vector_type(8))) __bf16 rbf16x8;
+typedef uint32_t ru32x4 __attribute__((ext_vector_type(4)));
+
+MOE_DEV f32x4 rmfma(ru32x4 a, ru32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(rbf16x8, a),
+                                                   __builtin_bit_cast(rbf16x8, b), c, 0, 0, 0);
+}
+
+// 8 fp32 weights -> their hi, mid and lo bf16 parts, packed in k order
+MOE_DEV void split3(const float (&w)[8], ru32x4& hi, ru32x4& mid, ru32x4& lo) {
+    uint32_t h[8], m[8], l[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t u = __float_as_uint(w[j]);
+        h[j] = u & 0xFFFF0000u;
+        const float r1 = w[j] - __uint_as_float(h[j]);       // exact
+        m[j] = __float_as_uint(r1) & 0xFFFF0000u;
+        const float r2 = r1 - __uint_as_float(m[j]);          // exact, at most 8 significant bits
+        l[j] = __float_as_uint(r2) & 0xFFFF0000u;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        hi[q] = (h[2 * q] >> 16) | h[2 * q + 1];
+        mid[q] = (m[2 * q] >> 16) | m[2 * q + 1];
+        lo[q] = (l[2 * q] >> 16) | l[2 * q + 1];
+    }
+}
+
+__global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __restrict__ x, int T, int H,
+                                                          const float* __restrict__ W,
+                                                          const float* __restrict__ rsc,
+                                                          const float* __restrict__ bias, int E,
+                                                          float* __restrict__ logits) {
+    __shared__ f32x4 part[3][4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int t0 = blockIdx.x * 32;
+    const int e0 = blockIdx.y * 32;
+    // this wave's quarter of H (H is a multiple of 32)
+    const int nsteps = H >> 5;
+    const int k_begin = (nsteps * wave / 4) * 32, k_end = (nsteps * (wave + 1) / 4) * 32;
+    // A operand: lane (token row l16, k group g); B operand: lane (expert column l16, k group g)
+    const uint16_t* xa = x + (int64_t)min(t0 + l16, T - 1) * H + 8 * g;
+    const uint16_t* xb = x + (int64_t)min(t0 + 16 + l16, T - 1) * H + 8 * g;
+    const float* w0 = W + (int64_t)(e0 + l16) * H + 8 * g;
+    const float* w1 = W + (int64_t)(e0 + 16 + l16) * H + 8 * g;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc2 = {0.f, 0.f, 0.f, 0.f}, acc3 = {0.f, 0.f, 0.f, 0.f};  // second token fragment
+    // the loads of step k+32 are issued before the MFMAs of step k (clamped at the end)
+    struct Step {
+        ru32x4 a, b;
+        float4 p0, p1, q0, q1, s0, s1;
+    };
+    auto load = [&](Step& S, int k) {
+        S.a = *(const ru32x4*)(xa + k);
+        S.b = *(const ru32x4*)(xb + k);
+        S.p0 = *(const float4*)(w0 + k);
+        S.p1 = *(const float4*)(w0 + k + 4);
+        S.q0 = *(const float4*)(w1 + k);
+        S.q1 = *(const float4*)(w1 + k + 4);
+        if (rsc) {
+            S.s0 = *(const float4*)(rsc + 8 * g + k);
+            S.s1 = *(const float4*)(rsc + 8 * g + k + 4);
+        }
+    };
+    Step cur, nxt;
+    load(cur, min(k_begin, H - 32));
+    for (int k = k_begin; k < k_end; k += 32) {
+        load(nxt, min(k + 32, H - 32));
+        float wa[8] = {cur.p0.x, cur.p0.y, cur.p0.z, cur.p0.w, cur.p1.x, cur.p1.y, cur.p1.z, cur.p1.w};
+        float wb[8] = {cur.q0.x, cur.q0.y, cur.q0.z, cur.q0.w, cur.q1.x, cur.q1.y, cur.q1.z, cur.q1.w};
+        if (rsc) {
+            const float sv[8] = {cur.s0.x, cur.s0.y, cur.s0.z, cur.s0.w,
+                                 cur.s1.x, cur.s1.y, cur.s1.z, cur.s1.w};
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                wa[jj] *= sv[jj];
+                wb[jj] *= sv[jj];
+            }
+        }
+        ru32x4 h0, m0, lo0, h1, m1, lo1;
+        split3(wa, h0, m0, lo0);
+        split3(wb, h1, m1, lo1);
+        acc0 = rmfma(cur.a, h0, acc0);
+        acc1 = rmfma(cur.a, h1, acc1);
+        acc2 = rmfma(cur.b, h0, acc2);
+        acc3 = rmfma(cur.b, h1, acc3);
+        acc0 = rmfma(cur.a, m0, acc0);
+        acc1 = rmfma(cur.a, m1, acc1);
+        acc2 = rmfma(cur.b, m0, acc2);
+        acc3 = rmfma(cur.b, m1, acc3);
+        acc0 = rmfma(cur.a, lo0, acc0);
+        acc1 = rmfma(cur.a, lo1, acc1);
+        acc2 = rmfma(cur.b, lo0, acc2);
+        acc3 = rmfma(cur.b, lo1, acc3);
+        cur = nxt;
+    }
+    // partial sums of waves 1..3 to LDS; wave 0 adds them in order and stores
+    if (wave > 0) {
+        part[wave - 1][0][lane] = acc0;
+        part[wave - 1][1][lane] = acc1;
+        part[wave - 1][2][lane] = acc2;
+        part[wave - 1][3][lane] = acc3;
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+        acc0 += part[w][0][lane];
+        acc1 += part[w][1][lane];
+        acc2 += part[w][2][lane];
+        acc3 += part[w][3][lane];
+    }
+    // output lane (token rows 4g..4g+3, expert column l16)
+    const float b0 = bias ? bias[e0 + l16] : 0.f, b1 = bias ? bias[e0 + 16 + l16] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 4 * g + i;
+        if (t < T) {
+            logits[(int64_t)t * E + e0 + l16] = acc0[i] + b0;
+            logits[(int64_t)t * E + e0 + 16 + l16] = acc1[i] + b1;
+        }
+        if (t + 16 < T) {
+            logits[(int64_t)(t + 16) * E + e0 + l16] = acc2[i] + b0;
+            logits[(int64_t)(t + 16) * E + e0 + 16 + l16] = acc3[i] + b1;
+        }
+    }
+}
+
 hipError_t launch_router_logits(const void* x, int x_dt, int64_t T, int H, const float* W,
                                 const float* rsc, const float* bias, int E, float* logits,
                                 hipStream_t st) {
-    if (T <= ROUTER_GEMV_MAX_T) {
+    if (x_dt == MOE_BF16 && T >= ROUTER_MFMA_MIN_T && E % 32 == 0) {
+        dim3 grid((unsigned)((T + 31) / 32), E / 32);
+        router_logits_mfma<<<grid, 256, 0, st>>>((const uint16_t*)x, (int)T, H, W, rsc, bias, E,
+                                                 logits);
+    } else if (T <= ROUTER_GEMV_MAX_T) {
         dim3 grid((E + 3) / 4);
         if (x_dt == MOE_F32)
             router_logits_gemv<MOE_F32><<<grid, 256, 0, st>>>(x, (int)T, H, W, rsc, bias, E, logits);
