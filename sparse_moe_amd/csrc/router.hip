@@ -20,45 +20,73 @@ MOE_DEV float4 load_x4(const void* x, int xdt, int64_t i4) {
                        __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
 }
 
+// One expert per workgroup: wave w takes a quarter of the float4 chunks of the
+// expert's W_r row, dots them with every token (all loads issued before the
+// reductions) and leaves its per-token partial sums in part[w][t].
+template <int XDT>
+MOE_DEV void expert_partials(const void* __restrict__ x, int T, int H, const float* __restrict__ W,
+                             const float* __restrict__ rsc, int e,
+                             float (*part)[ROUTER_GEMV_MAX_T]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int H4 = H >> 2, nch = (H4 + 63) >> 6;
+    const int c0 = wave * nch / 4, c1 = (wave + 1) * nch / 4;
+    const float4* wr = reinterpret_cast<const float4*>(W + (int64_t)e * H);
+    constexpr int CPW = ROUTER_MAX_CHUNKS / 4;
+    float4 wv[CPW];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        const int c = c0 + i;
+        wv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (c < c1) {
+            const int j4 = min(lane + 64 * c, H4 - 1);
+            wv[i] = wr[j4];
+            if (rsc) {
+                const float4 sv = reinterpret_cast<const float4*>(rsc)[j4];
+                wv[i].x *= sv.x; wv[i].y *= sv.y; wv[i].z *= sv.z; wv[i].w *= sv.w;
+            }
+            if (lane + 64 * c >= H4) wv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+    float acc[ROUTER_GEMV_MAX_T];
+#pragma unroll
+    for (int t = 0; t < ROUTER_GEMV_MAX_T; ++t) acc[t] = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        const int c = c0 + i;
+        if (c < c1) {
+            const int j4 = min(lane + 64 * c, H4 - 1);
+#pragma unroll
+            for (int t = 0; t < ROUTER_GEMV_MAX_T; ++t) {
+                if (t < T) {
+                    const float4 xv = load_x4(x, XDT, (int64_t)t * H4 + j4);
+                    acc[t] = fmaf(xv.x, wv[i].x, acc[t]);
+                    acc[t] = fmaf(xv.y, wv[i].y, acc[t]);
+                    acc[t] = fmaf(xv.z, wv[i].z, acc[t]);
+                    acc[t] = fmaf(xv.w, wv[i].w, acc[t]);
+                }
+            }
+        }
+    }
+    for (int t = 0; t < T; ++t) {
+        const float sum = wave_sum(acc[t]);
+        if (lane == 0) part[wave][t] = sum;
+    }
+}
+
 template <int XDT>
 __global__ __launch_bounds__(256) void router_logits_gemv(const void* __restrict__ x, int T, int H,
                                                           const float* __restrict__ W,
                                                           const float* __restrict__ rsc,
                                                           const float* __restrict__ bias, int E,
                                                           float* __restrict__ logits) {
-    const int lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (e >= E) return;
-    const float* w = W + (int64_t)e * H;
-    const int H4 = H >> 2;
-    float4 wv[ROUTER_MAX_CHUNKS];
-#pragma unroll
-    for (int c = 0; c < ROUTER_MAX_CHUNKS; ++c) {
-        const int j4 = min(lane + 64 * c, H4 - 1);
-        wv[c] = reinterpret_cast<const float4*>(w)[j4];
-        if (lane + 64 * c >= H4) wv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    if (rsc) {
-#pragma unroll
-        for (int c = 0; c < ROUTER_MAX_CHUNKS; ++c) {
-            const float4 sv = reinterpret_cast<const float4*>(rsc)[min(lane + 64 * c, H4 - 1)];
-            wv[c].x *= sv.x; wv[c].y *= sv.y; wv[c].z *= sv.z; wv[c].w *= sv.w;
-        }
-    }
-    const float b = bias ? bias[e] : 0.f;
-    for (int t = 0; t < T; ++t) {
-        float acc = 0.f;
-#pragma unroll
-        for (int c = 0; c < ROUTER_MAX_CHUNKS; ++c) {
-            const float4 xv = load_x4(x, XDT, (int64_t)t * H4 + min(lane + 64 * c, H4 - 1));
-            acc = fmaf(xv.x, wv[c].x, acc);
-            acc = fmaf(xv.y, wv[c].y, acc);
-            acc = fmaf(xv.z, wv[c].z, acc);
-            acc = fmaf(xv.w, wv[c].w, acc);
-        }
-        const float s = wave_sum(acc);
-        if (lane == 0) logits[(int64_t)t * E + e] = s + b;
-    }
+    __shared__ float part[4][ROUTER_GEMV_MAX_T];
+    const int e = blockIdx.x;
+    expert_partials<XDT>(x, T, H, W, rsc, e, part);
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < T)
+        logits[(int64_t)t * E + e] =
+            ((part[0][t] + part[1][t]) + (part[2][t] + part[3][t])) + (bias ? bias[e] : 0.f);
 }
 
 // ---------------------------------------------------------------------------
@@ -156,38 +184,17 @@ __global__ __launch_bounds__(256) void route_small(const void* __restrict__ x, i
                                                    int32_t* __restrict__ sorted_slots,
                                                    int32_t* __restrict__ slot_pos,
                                                    int* __restrict__ counter) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int e = blockIdx.x * 4 + wave;
-    if (e < E) {
-        const float* wr = W + (int64_t)e * H;
-        const int H4 = H >> 2;
-        float4 wv[ROUTER_MAX_CHUNKS];
-#pragma unroll
-        for (int c = 0; c < ROUTER_MAX_CHUNKS; ++c) {
-            wv[c] = reinterpret_cast<const float4*>(wr)[min(lane + 64 * c, H4 - 1)];
-            if (lane + 64 * c >= H4) wv[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        if (rsc) {
-#pragma unroll
-            for (int c = 0; c < ROUTER_MAX_CHUNKS; ++c) {
-                const float4 sv = reinterpret_cast<const float4*>(rsc)[min(lane + 64 * c, H4 - 1)];
-                wv[c].x *= sv.x; wv[c].y *= sv.y; wv[c].z *= sv.z; wv[c].w *= sv.w;
-            }
-        }
-        const float b = bias ? bias[e] : 0.f;
-        for (int t = 0; t < T; ++t) {
-            float acc = 0.f;
-#pragma unroll
-            for (int c = 0; c < ROUTER_MAX_CHUNKS; ++c) {
-                const float4 xv = load_x4(x, XDT, (int64_t)t * H4 + min(lane + 64 * c, H4 - 1));
-                acc = fmaf(xv.x, wv[c].x, acc);
-                acc = fmaf(xv.y, wv[c].y, acc);
-                acc = fmaf(xv.z, wv[c].z, acc);
-                acc = fmaf(xv.w, wv[c].w, acc);
-            }
-            const float s = wave_sum(acc);
-            if (lane == 0) coherent_store(logits + (int64_t)t * E + e, s + b);
-        }
+    const int wave = threadIdx.x >> 6;
+    __shared__ float part[4][ROUTER_GEMV_MAX_T];
+    const int e = blockIdx.x;  // one expert per workgroup, H split over its waves
+    expert_partials<XDT>(x, T, H, W, rsc, e, part);
+    __syncthreads();
+    {
+        const int t = threadIdx.x;
+        if (t < T)
+            coherent_store(logits + (int64_t)t * E + e,
+                           ((part[0][t] + part[1][t]) + (part[2][t] + part[3][t])) +
+                               (bias ? bias[e] : 0.f));
     }
     __shared__ int s_last;
     drain_stores();
@@ -209,7 +216,7 @@ hipError_t launch_route_small(const void* x, int x_dt, int T, int H, const float
                               const float* rsc, const float* bias, int E, int K, float* logits,
                               int32_t* ids, float* w, int32_t* offsets, int32_t* sorted_slots,
                               int32_t* slot_pos, int* counter, hipStream_t st) {
-    dim3 grid((E + 3) / 4);
+    dim3 grid(E);
     if (x_dt == MOE_F32)
         route_small<MOE_F32><<<grid, 256, 0, st>>>(x, T, H, W, rsc, bias, E, K, logits, ids, w,
                                                    offsets, sorted_slots, slot_pos, counter);
@@ -367,7 +374,7 @@ hipError_t launch_router_logits(const void* x, int x_dt, int64_t T, int H, const
         router_logits_mfma<<<grid, 256, 0, st>>>((const uint16_t*)x, (int)T, H, W, rsc, bias, E,
                                                  logits);
     } else if (T <= ROUTER_GEMV_MAX_T) {
-        dim3 grid((E + 3) / 4);
+        dim3 grid(E);
         if (x_dt == MOE_F32)
             router_logits_gemv<MOE_F32><<<grid, 256, 0, st>>>(x, (int)T, H, W, rsc, bias, E, logits);
         else
