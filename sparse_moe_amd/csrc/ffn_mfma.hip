@@ -68,11 +68,18 @@ MOE_DEV f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Tile lookup: tiles are numbered expert by expert, ceil(count/MT) per expert.
-// Wave 0 scans the expert counts (up to 4 experts per lane); returns false for
-// a tile number past the last tile.
-__device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int tile, int* s_res,
-                          int& e_out, int& base, int& cnt) {
+// Tile lookup.  Slot tiles are numbered expert by expert, ceil(count/MT) per
+// expert; each slot tile has n_tiles column tiles.  The grid is
+// an upper bound on the tile count, so the numbering is made once the real
+// count is known: the tiles are cut into 8 equal runs of consecutive numbers,
+// run x going to the workgroups that the dispatcher places on XCD x (block
+// numbers congruent to x mod 8).  The column tiles of one slot tile, and the
+// next slot tile of the same expert, thus share an XCD's L2, and every XCD
+// gets an equal share however many tiles there are.  Wave 0 scans the expert
+// counts (up to 4 experts per lane); returns false for a workgroup without a
+// tile.
+__device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
+                          int n_tiles, int* s_res, int& e_out, int& base, int& cnt, int& ntile) {
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
         int c[4], t[4], tot = 0;
@@ -89,6 +96,11 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int tile, 
             const int v = __shfl_up(incl, d);
             if (lane >= d) incl += v;
         }
+        const int total = __shfl(incl, 63) * n_tiles;
+        const int per_xcd = (total + 7) >> 3;
+        const int lin = (bid & 7) * per_xcd + (bid >> 3);
+        const bool have = (bid >> 3) < per_xcd && lin < total;
+        const int tile = have ? lin / n_tiles : -1;
         int run = incl - tot;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -97,15 +109,17 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int tile, 
                 s_res[0] = e;
                 s_res[1] = offsets[e] + k * MT;
                 s_res[2] = min(MT, c[q] - k * MT);
+                s_res[3] = lin - tile * n_tiles;
             }
             run += t[q];
         }
-        if (lane == 63 && tile >= incl) s_res[0] = -1;
+        if (lane == 63 && !have) s_res[0] = -1;
     }
     __syncthreads();
     e_out = s_res[0];
     base = s_res[1];
     cnt = s_res[2];
+    ntile = s_res[3];
     return e_out >= 0;
 }
 
@@ -134,22 +148,18 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int tile, 
 template <int MODE>
 __global__ __launch_bounds__(256) void ffn_mfma(
     const uint16_t* __restrict__ act, const float* __restrict__ csum, const uint8_t* __restrict__ W,
-    int nb, int rows_e, int ncols, int n_tiles, int tiles_per_xcd, const int32_t* __restrict__ offsets,
+    int nb, int rows_e, int ncols, int n_tiles, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_slots, int K, int E, uint16_t* __restrict__ h_out,
     float* __restrict__ hsum_out, float* __restrict__ y_out) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    __shared__ int s_res[3];
+    __shared__ int s_res[4];
 
-    // XCD-aware numbering: consecutive tile numbers (the column tiles of one
-    // slot tile, then the next slot tile of the same expert) share an XCD's L2.
-    const int bid = blockIdx.x;
-    const int lin = (bid & 7) * tiles_per_xcd + (bid >> 3);
-    const int mtile = lin / n_tiles, ntile = lin - mtile * n_tiles;
-    int e, base, cnt;
-    if (!find_tile(offsets, E, mtile, s_res, e, base, cnt)) return;
+    int e, base, cnt, ntile;
+    if (!find_tile(offsets, E, blockIdx.x, n_tiles, s_res, e, base, cnt, ntile)) return;
     e = __builtin_amdgcn_readfirstlane(e);
     base = __builtin_amdgcn_readfirstlane(base);
     cnt = __builtin_amdgcn_readfirstlane(cnt);
+    ntile = __builtin_amdgcn_readfirstlane(ntile);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -412,21 +422,20 @@ hipError_t launch_ffn_mfma(const void* x, int64_t T, int H, const uint8_t* w_gat
     const int64_t nblk = T * (H / 32);
     ffn_mfma_prep<<<(unsigned)((nblk + 255) / 256), 256, 0, st>>>((const uint16_t*)x, nblk, xp, xs);
 
-    // slot tiles: sum over experts of ceil(count / MT) <= N / MT + (experts hit)
+    // slot tiles: sum over experts of ceil(count / MT) <= N / MT + (experts hit);
+    // the workgroups past the real count exit at once
     const int mtiles = N / MT + min(E, N);
     {
         const int n_tiles = (I + NT / 2 - 1) / (NT / 2);
         const int total = (mtiles * n_tiles + 7) / 8 * 8;
         ffn_mfma<0><<<total, 256, LDS_BYTES, st>>>(xp, xs, w_gate_up, H / 32, 2 * I, I, n_tiles,
-                                                   total / 8, offsets, sorted_slots, K, E, hp, hs,
-                                                   nullptr);
+                                                   offsets, sorted_slots, K, E, hp, hs, nullptr);
     }
     {
         const int n_tiles = (H + NT - 1) / NT;
         const int total = (mtiles * n_tiles + 7) / 8 * 8;
-        ffn_mfma<1><<<total, 256, LDS_BYTES, st>>>(hp, hs, w_down, I / 32, H, H, n_tiles, total / 8,
-                                                   offsets, sorted_slots, K, E, nullptr, nullptr,
-                                                   y_sorted);
+        ffn_mfma<1><<<total, 256, LDS_BYTES, st>>>(hp, hs, w_down, I / 32, H, H, n_tiles, offsets,
+                                                   sorted_slots, K, E, nullptr, nullptr, y_sorted);
     }
     return hipGetLastError();
 }

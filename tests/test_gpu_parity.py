@@ -122,16 +122,25 @@ def test_deterministic_and_fully_written():
         assert np.array_equal(outs[0][k].view(np.uint8), outs[1][k].view(np.uint8)), k
 
 
-@pytest.mark.parametrize("H,I,E,K,T", [
-    (288, 96, 8, 2, 70),       # odd block counts per row (9 and 3): served by the GEMV path
-    (256, 64, 8, 2, 600),      # ~150 slots per expert: two slot tiles per expert
-    (256, 192, 4, 1, 300),     # K = 1, a partial second column tile of the gate/up product
-    (2816, 704, 128, 8, 64),   # Gemma shape at the smallest token count of the MFMA path
+@pytest.mark.parametrize("H,I,E,K,T,zipf", [
+    (288, 96, 8, 2, 70, None),       # odd block counts per row (9 and 3): served by the GEMV path
+    (256, 64, 8, 2, 600, None),      # ~150 slots per expert: two slot tiles per expert
+    (256, 192, 4, 1, 300, None),     # K = 1, a partial second column tile of the gate/up product
+    (2816, 704, 128, 8, 64, None),   # Gemma shape at the smallest token count of the MFMA path
+    # Zipf-skewed routing: experts of a few slots (one mostly empty tile) next
+    # to experts of several tiles, as in the layer stack
+    (512, 128, 32, 4, 256, 1.1),
 ])
-def test_mfma_path_shapes(H, I, E, K, T):
+def test_mfma_path_shapes(H, I, E, K, T, zipf):
     # bf16 activations with T >= 64 take the bf16 MFMA grouped GEMM
     spec = synth.LayerSpec("mfma-H%d-I%d-E%d-K%d-T%d" % (H, I, E, K, T), H=H, E=E, K=K, I=I, T=T,
-                           act="bf16", router_std=1 / np.sqrt(H), seed=11)
+                           act="bf16", router_std=1 / np.sqrt(H), seed=11, zipf_s=zipf)
     L = synth.make_layer(spec)
+    if zipf is not None:
+        # the routing really mixes experts of at most 16 slots with experts of
+        # more than one 128-slot tile
+        ids, _ = oracle.topk_softmax(oracle.router_logits(L.x, L.w_router, bias=L.router_bias), K)
+        counts = np.bincount(ids.ravel(), minlength=E)
+        assert ((counts > 0) & (counts <= 16)).any() and (counts > 128).any(), counts
     sample = None if H < 1024 else np.arange(0, T, 5)
     _run(L, token_sample=sample)
