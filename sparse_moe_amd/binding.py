@@ -195,6 +195,38 @@ def moe_expert_ffn_q4_0(x: torch.Tensor, w_gate_up: torch.Tensor, w_down: torch.
            "moe_expert_ffn_q4_0")
 
 
+_DENSE_INDEX = {}
+
+
+def dense_ffn_q4_0(x: torch.Tensor, w_gate_up: torch.Tensor, w_down: torch.Tensor,
+                   out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """The block's dense MLP: out = (GELU_tanh(x Wg^T) * (x Wu^T)) Wd^T in fp32.
+
+    Model card "Gemma 4 26B-A4B it QAT Q4_0 with MTP assistant and vision, NInfer
+    v3 artifact", table "What is inside": the dense MLP's gate and up rows form
+    one Q4_0 parent, like an expert's.  It runs as an always-on expert: one
+    expert, top-1, weight 1, so the slot order is the token order and the
+    expert FFN's per-slot output is the result (no combine).  w_gate_up is
+    uint8 [2I, H/32, 18] (or [1, 2I, H/32, 18]), w_down uint8 [H, I/32, 18]."""
+    T, H = x.shape
+    gu = w_gate_up.reshape(1, -1, H // 32, 18)
+    dn = w_down.reshape(1, H, -1, 18)
+    I = gu.shape[1] // 2
+    key = (x.device, T)
+    if key not in _DENSE_INDEX:
+        _DENSE_INDEX[key] = (torch.tensor([0, T], dtype=torch.int32, device=x.device),
+                             torch.arange(T, dtype=torch.int32, device=x.device))
+    offsets, slots = _DENSE_INDEX[key]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    if ws is None:
+        nb = max(16, moe_expert_ffn_q4_0_workspace_bytes(T, 1, H, I, 1, act_dtype(x)))
+        ws = torch.empty((nb,), dtype=torch.uint8, device=x.device)
+    moe_expert_ffn_q4_0(x, gu, dn, 1, offsets, slots, out, ws, stream=stream)
+    return out
+
+
 def moe_combine(y_sorted: torch.Tensor, slot_pos: torch.Tensor, topk_ids: torch.Tensor,
                 topk_w: torch.Tensor, expert_scale: Optional[torch.Tensor] = None,
                 out_f32: Optional[torch.Tensor] = None, out_act: Optional[torch.Tensor] = None,

@@ -26,6 +26,8 @@
 // a wave's 64 rows are 32 gate rows and the 32 up rows of the same hidden
 // columns, so each lane holds gate and up of the same (slot, column) in
 // matching registers and GELU(g) * u is formed in the epilogue.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace moe {
@@ -198,48 +200,19 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
         aoff[i] = (uint32_t)(arow * nb * 32) + 8u * (uint32_t)ch;
     }
-    uint32_t coff;  // block-sum offset of tile row (tid & 127)
+    uint32_t coff;  // block-sum offset of (tile row tid & 127, block tid >> 7 of a pair)
     {
         const int r = tid & (MT - 1);
         const int p = base + min(r, cnt - 1);
         const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
-        coff = (uint32_t)(arow * nb);
+        coff = (uint32_t)(arow * nb) + (uint32_t)(tid >> 7);
     }
 
     const int mfa = min(8, (cnt + 15) >> 4);  // valid slot fragments
     const bool active = nfa > 0;
 
-    f32x4 acc[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int jn = 0; jn < 4; ++jn) acc[i][jn] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-    struct AStage {
-        u32x4a4 a[4];
-        float c0, c1;
-    };
     struct BStage {
         uint32_t lo[4], hi[4], q1[4];
-    };
-    auto load_a = [&](AStage& S, int j) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S.a[i] = *(const u32x4a4*)(act + aoff[i] + (uint32_t)j * 64u);
-        const float* cp = csum + coff + 2u * (uint32_t)j;
-        S.c0 = cp[0];
-        S.c1 = cp[1];
-    };
-    auto store_a = [&](const AStage& S, int slot) {
-        uint8_t* A_lds = smem + slot * SLOT_BYTES;
-        float* C_lds = (float*)(A_lds + 2 * MT * ROWB);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *(u32x4*)(A_lds + ((ch >> 2) * MT + srow + 32 * i) * ROWB + 16 * (ch & 3)) =
-                (u32x4){S.a[i].x, S.a[i].y, S.a[i].z, S.a[i].w};
-        if (tid < MT) {
-            C_lds[tid] = S.c0;
-            C_lds[MT + tid] = S.c1;
-        }
     };
     auto load_b = [&](BStage& S, int j) {
 #pragma unroll
@@ -251,114 +224,151 @@ __global__ __launch_bounds__(256) void ffn_mfma(
             S.q1[nf] = *(const uint32_t*)(wp + 20);  // qs1 bytes 4g .. 4g+3
         }
     };
-    auto compute = [&](int slot, const BStage& S) {
-        const uint8_t* A_lds = smem + slot * SLOT_BYTES;
-        const float* C_lds = (const float*)(A_lds + 2 * MT * ROWB);
+
+    // The main loop and epilogue for MF slot fragments (16 slots each).  A tile
+    // of at most 32 slots (an expert's last, partial tile, or a small expert)
+    // runs with MF = 2: a quarter of the activation staging, MFMAs and scale
+    // FMAs of a full tile.
+    auto run = [&](auto mf_const) {
+        constexpr int MF = decltype(mf_const)::value;
+        constexpr int NA = MF / 2;  // activation chunks per thread per pair (32 rows each)
+        f32x4 acc[MF][4];
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            // this block's weights: unpack the lane's qs dword, fetch the scale of
-            // its row from the lane of group 0 (block 0) or group 3 (block 1)
-            float dv[4];
-            u32x4 bq[4];
+        for (int i = 0; i < MF; ++i)
 #pragma unroll
-            for (int nf = 0; nf < 4; ++nf) {
-                if (blk == 0) {
-                    const uint32_t d0 = (uint32_t)__shfl((int)S.lo[nf], l16);
-                    dv[nf] = f16_bits_to_f32(d0 & 0xFFFFu);
-                    bq[nf] = dq_group(__builtin_amdgcn_alignbyte(S.hi[nf], S.lo[nf], 2));
-                } else {
-                    const uint32_t d1 = (uint32_t)__shfl((int)S.hi[nf], 48 + l16);
-                    dv[nf] = f16_bits_to_f32(d1 >> 16);
-                    bq[nf] = dq_group(S.q1[nf]);
+            for (int jn = 0; jn < 4; ++jn) acc[i][jn] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+        struct AStage {
+            u32x4a4 a[NA];
+            float c;
+        };
+        auto load_a = [&](AStage& S, int j) {
+#pragma unroll
+            for (int i = 0; i < NA; ++i) S.a[i] = *(const u32x4a4*)(act + aoff[i] + (uint32_t)j * 64u);
+            S.c = csum[coff + 2u * (uint32_t)j];
+        };
+        auto store_a = [&](const AStage& S, int slot) {
+            uint8_t* A_lds = smem + slot * SLOT_BYTES;
+            float* C_lds = (float*)(A_lds + 2 * MT * ROWB);
+#pragma unroll
+            for (int i = 0; i < NA; ++i)
+                *(u32x4*)(A_lds + ((ch >> 2) * MT + srow + 32 * i) * ROWB + 16 * (ch & 3)) =
+                    (u32x4){S.a[i].x, S.a[i].y, S.a[i].z, S.a[i].w};
+            C_lds[tid] = S.c;  // block tid >> 7, row tid & 127
+        };
+        auto compute = [&](int slot, const BStage& S) {
+            const uint8_t* A_lds = smem + slot * SLOT_BYTES;
+            const float* C_lds = (const float*)(A_lds + 2 * MT * ROWB);
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                // this block's weights: unpack the lane's qs dword, fetch the scale of
+                // its row from the lane of group 0 (block 0) or group 3 (block 1)
+                float dv[4];
+                u32x4 bq[4];
+#pragma unroll
+                for (int nf = 0; nf < 4; ++nf) {
+                    if (blk == 0) {
+                        const uint32_t d0 = (uint32_t)__shfl((int)S.lo[nf], l16);
+                        dv[nf] = f16_bits_to_f32(d0 & 0xFFFFu);
+                        bq[nf] = dq_group(__builtin_amdgcn_alignbyte(S.hi[nf], S.lo[nf], 2));
+                    } else {
+                        const uint32_t d1 = (uint32_t)__shfl((int)S.hi[nf], 48 + l16);
+                        dv[nf] = f16_bits_to_f32(d1 >> 16);
+                        bq[nf] = dq_group(S.q1[nf]);
+                    }
+                    // keep the scale a plain fp32 register: otherwise the compiler folds
+                    // the fp16 conversion into v_fma_mix_f32 for every scale FMA, which
+                    // issues slower and raises register pressure into spills
+                    asm volatile("" : "+v"(dv[nf]));
                 }
-                // keep the scale a plain fp32 register: otherwise the compiler folds
-                // the fp16 conversion into v_fma_mix_f32 for every scale FMA, which
-                // issues slower and raises register pressure into spills
-                asm volatile("" : "+v"(dv[nf]));
+                // every slot fragment, unconditionally (rows past the count are computed
+                // and dropped at the store): per-fragment branches cost registers and
+                // serialise the schedule
+#pragma unroll
+                for (int mf = 0; mf < MF; ++mf) {
+                    const int r = blk * MT + mf * 16;
+                    const u32x4 a = *(const u32x4*)(A_lds + (r + l16) * ROWB + 16 * g);
+                    const f32x4 c = *(const f32x4*)&C_lds[r + 4 * g];
+                    f32x4 t[4];
+#pragma unroll
+                    for (int nf = 0; nf < 4; ++nf) t[nf] = mfma_bf16(a, bq[nf], c);
+#pragma unroll
+                    for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[mf][nf][i] = fmaf(dv[nf], t[nf][i], acc[mf][nf][i]);
+                }
             }
-            // every slot fragment, unconditionally (rows past the count are computed
-            // and dropped at the store): per-fragment branches cost registers and
-            // serialise the schedule
+        };
+
+        AStage RA;
+        BStage RB;
+        load_a(RA, 0);
+        load_b(RB, 0);
+        store_a(RA, 0);
+        load_a(RA, min(1, npairs - 1));
+        lds_barrier();
+        for (int j = 0; j < npairs; ++j) {
+            store_a(RA, (j + 1) & 1);
+            load_a(RA, min(j + 2, npairs - 1));
+            if (active) compute(j & 1, RB);
+            load_b(RB, min(j + 1, npairs - 1));
+            lds_barrier();
+        }
+
+        if (!active) return;
+        if (MODE == 0) {
+            // h = GELU(g) * u for hidden columns c0 .. c0+31: one Q4_0 block of the
+            // down product's K, written in the MFMA order with its sum.
+            const int I = ncols, nbh = I >> 5;
+            const int hblk = c0 >> 5;
 #pragma unroll
-            for (int mf = 0; mf < 8; ++mf) {
-                const int r = blk * MT + mf * 16;
-                const u32x4 a = *(const u32x4*)(A_lds + (r + l16) * ROWB + 16 * g);
-                const f32x4 c = *(const f32x4*)&C_lds[r + 4 * g];
-                f32x4 t[4];
+            for (int mf = 0; mf < MF; ++mf) {
+                if (mf < mfa) {
 #pragma unroll
-                for (int nf = 0; nf < 4; ++nf) t[nf] = mfma_bf16(a, bq[nf], c);
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = mf * 16 + 4 * g + i;
+                        const bool ok = r < cnt;
+                        const int64_t p = base + min(r, cnt - 1);
+                        float s = 0.f;
 #pragma unroll
-                for (int nf = 0; nf < 4; ++nf)
+                        for (int f = 0; f < 2; ++f) {
+                            const float gv = 16.f * acc[mf][f][i], uv = 16.f * acc[mf][2 + f][i];
+                            const uint16_t hb = f32_to_bf16(gelu_tanh(gv) * uv);
+                            s += bf16_to_f32(hb);
+                            if (ok) h_out[p * I + hblk * 32 + perm_pos(f * 16 + l16)] = hb;
+                        }
+                        // sum over the 16 lanes holding this row's columns
+                        s += dpp_f32<DPP_QUAD_XOR1>(0.f, s);
+                        s += dpp_f32<DPP_QUAD_XOR2>(0.f, s);
+                        s += dpp_f32<DPP_ROW_HALF_MIRROR>(0.f, s);
+                        s += dpp_f32<DPP_ROW_MIRROR>(0.f, s);
+                        if (ok && l16 == 0) hsum_out[p * nbh + hblk] = -1.5f * s;
+                    }
+                }
+            }
+        } else {
+            const int H = ncols;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[mf][nf][i] = fmaf(dv[nf], t[nf][i], acc[mf][nf][i]);
+            for (int mf = 0; mf < MF; ++mf) {
+                if (mf < mfa) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = mf * 16 + 4 * g + i;
+                        if (r < cnt) {
+                            float* yp = y_out + (int64_t)(base + r) * H + c0 + l16;
+#pragma unroll
+                            for (int nf = 0; nf < 4; ++nf)
+                                if (nf < nfa) yp[nf * 16] = 16.f * acc[mf][nf][i];
+                        }
+                    }
+                }
             }
         }
     };
-
-    AStage RA;
-    BStage RB;
-    load_a(RA, 0);
-    load_b(RB, 0);
-    store_a(RA, 0);
-    load_a(RA, min(1, npairs - 1));
-    lds_barrier();
-    for (int j = 0; j < npairs; ++j) {
-        store_a(RA, (j + 1) & 1);
-        load_a(RA, min(j + 2, npairs - 1));
-        if (active) compute(j & 1, RB);
-        load_b(RB, min(j + 1, npairs - 1));
-        lds_barrier();
-    }
-
-    if (!active) return;
-    if (MODE == 0) {
-        // h = GELU(g) * u for hidden columns c0 .. c0+31: one Q4_0 block of the
-        // down product's K, written in the MFMA order with its sum.
-        const int I = ncols, nbh = I >> 5;
-        const int hblk = c0 >> 5;
-#pragma unroll
-        for (int mf = 0; mf < 8; ++mf) {
-            if (mf < mfa) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = mf * 16 + 4 * g + i;
-                    const bool ok = r < cnt;
-                    const int64_t p = base + min(r, cnt - 1);
-                    float s = 0.f;
-#pragma unroll
-                    for (int f = 0; f < 2; ++f) {
-                        const float gv = 16.f * acc[mf][f][i], uv = 16.f * acc[mf][2 + f][i];
-                        const uint16_t hb = f32_to_bf16(gelu_tanh(gv) * uv);
-                        s += bf16_to_f32(hb);
-                        if (ok) h_out[p * I + hblk * 32 + perm_pos(f * 16 + l16)] = hb;
-                    }
-                    // sum over the 16 lanes holding this row's columns
-                    s += dpp_f32<DPP_QUAD_XOR1>(0.f, s);
-                    s += dpp_f32<DPP_QUAD_XOR2>(0.f, s);
-                    s += dpp_f32<DPP_ROW_HALF_MIRROR>(0.f, s);
-                    s += dpp_f32<DPP_ROW_MIRROR>(0.f, s);
-                    if (ok && l16 == 0) hsum_out[p * nbh + hblk] = -1.5f * s;
-                }
-            }
-        }
-    } else {
-        const int H = ncols;
-#pragma unroll
-        for (int mf = 0; mf < 8; ++mf) {
-            if (mf < mfa) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = mf * 16 + 4 * g + i;
-                    if (r < cnt) {
-                        float* yp = y_out + (int64_t)(base + r) * H + c0 + l16;
-#pragma unroll
-                        for (int nf = 0; nf < 4; ++nf)
-                            if (nf < nfa) yp[nf * 16] = 16.f * acc[mf][nf][i];
-                    }
-                }
-            }
-        }
-    }
+    if (cnt <= 32)
+        run(std::integral_constant<int, 2>{});
+    else
+        run(std::integral_constant<int, 8>{});
 }
 
 // Activations -> MFMA block order, plus -1.5 * block sums.  One thread per

@@ -5,7 +5,7 @@
 
 namespace moe {
 
-constexpr int ROUTER_GEMV_MAX_T = 8;   // router: per-expert GEMV up to this many tokens
+constexpr int ROUTER_GEMV_MAX_T = 8;   // router: tokens per workgroup of the per-expert GEMV (T < 64)
 constexpr int ROUTER_MFMA_MIN_T = 64;  // router: bf16 MFMA (exact three-way weight split) from here
 constexpr int PERM_TILE = 1024;        // permutation: slots per tile (256 threads x 4)
 constexpr int DIGIT_NMAX = 30583;       // largest |n| with 4 balanced base-16 digits: 7*(1+16+256+4096)

@@ -9,8 +9,8 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Few tokens: one wave per expert streams its W_r row once (float4 loads, all
-// issued at once) and dots it with every token (T <= ROUTER_GEMV_MAX_T).
+// Few tokens: one workgroup per expert streams its W_r row once (float4 loads,
+// all issued at once) and dots it with up to ROUTER_GEMV_MAX_T tokens.
 constexpr int ROUTER_MAX_CHUNKS = MOE_MAX_H / 256;  // float4 chunks of 64 lanes per row
 
 MOE_DEV float4 load_x4(const void* x, int xdt, int64_t i4) {
@@ -73,6 +73,10 @@ MOE_DEV void expert_partials(const void* __restrict__ x, int T, int H, const flo
     }
 }
 
+// Workgroup (e, g): expert e for tokens 8g .. 8g+7.  A token's logit is the same
+// sequence of operations whatever T is and wherever the token sits in the batch
+// (the fused few-token kernel uses the same expert_partials and final sum), so
+// every T below ROUTER_MFMA_MIN_T routes a token exactly as T = 1 does.
 template <int XDT>
 __global__ __launch_bounds__(256) void router_logits_gemv(const void* __restrict__ x, int T, int H,
                                                           const float* __restrict__ W,
@@ -81,16 +85,20 @@ __global__ __launch_bounds__(256) void router_logits_gemv(const void* __restrict
                                                           float* __restrict__ logits) {
     __shared__ float part[4][ROUTER_GEMV_MAX_T];
     const int e = blockIdx.x;
-    expert_partials<XDT>(x, T, H, W, rsc, e, part);
+    const int t0 = blockIdx.y * ROUTER_GEMV_MAX_T, tg = min(ROUTER_GEMV_MAX_T, T - t0);
+    const void* xg = XDT == MOE_F32 ? (const void*)((const float*)x + (int64_t)t0 * H)
+                                    : (const void*)((const uint16_t*)x + (int64_t)t0 * H);
+    expert_partials<XDT>(xg, tg, H, W, rsc, e, part);
     __syncthreads();
     const int t = threadIdx.x;
-    if (t < T)
-        logits[(int64_t)t * E + e] =
+    if (t < tg)
+        logits[(int64_t)(t0 + t) * E + e] =
             ((part[0][t] + part[1][t]) + (part[2][t] + part[3][t])) + (bias ? bias[e] : 0.f);
 }
 
 // ---------------------------------------------------------------------------
-// Many tokens: 32 tokens x 64 experts per workgroup, K-tiles of 32 staged in LDS.
+// Many tokens (fp32 activations, or an expert count that is not a multiple of
+// 32): 32 tokens x 64 experts per workgroup, K-tiles of 32 staged in LDS.
 constexpr int RT_BM = 32, RT_BN = 64, RT_BK = 32;
 
 template <int XDT>
@@ -373,8 +381,8 @@ hipError_t launch_router_logits(const void* x, int x_dt, int64_t T, int H, const
         dim3 grid((unsigned)((T + 31) / 32), E / 32);
         router_logits_mfma<<<grid, 256, 0, st>>>((const uint16_t*)x, (int)T, H, W, rsc, bias, E,
                                                  logits);
-    } else if (T <= ROUTER_GEMV_MAX_T) {
-        dim3 grid(E);
+    } else if (T < ROUTER_MFMA_MIN_T) {
+        dim3 grid(E, (unsigned)((T + ROUTER_GEMV_MAX_T - 1) / ROUTER_GEMV_MAX_T));
         if (x_dt == MOE_F32)
             router_logits_gemv<MOE_F32><<<grid, 256, 0, st>>>(x, (int)T, H, W, rsc, bias, E, logits);
         else
