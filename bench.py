@@ -14,6 +14,8 @@ single-threaded CPU oracle's rate on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +28,11 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 METRIC = "MoE-layer tokens/sec at 1 MI355X; decode HBM GB/s %peak, prefill MFMA %peak"
 Q4_0_EXPERT_BYTES = lambda H, I: 3 * H * I // 32 * 18   # [gate; up] + down
+# sources of the expert-FFN kernels: stored PMC traffic is reported only while
+# they are unchanged
+FFN_SOURCES = ("sparse_moe_amd/csrc/ffn_gemv.hip", "sparse_moe_amd/csrc/ffn_mfma.hip",
+               "sparse_moe_amd/csrc/common.h", "sparse_moe_amd/csrc/kernels.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_traffic.json")
 
 
 def parse():
@@ -39,7 +46,107 @@ def parse():
     p.add_argument("--sets", type=int, default=0, help="weight sets rotated (0: auto)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="first copy MIB MiB device to device (a dispatch of known size for "
+                        "scaling FETCH_SIZE / WRITE_SIZE counters)")
+    # no-GPU helpers that turn rocprofv3 output into the summaries kept in profiles/
+    p.add_argument("--summarize-stats", nargs=4, metavar=("CSV_DIR", "OUT_MD", "TITLE", "CMD"),
+                   help="write a markdown summary of a --kernel-trace --stats run")
+    p.add_argument("--summarize-traffic", nargs=4,
+                   metavar=("FETCH_DIR", "WRITE_DIR", "CALIB_MIB", "CMD"),
+                   help="store the expert-FFN HBM traffic per call of --config's workload from "
+                        "two --pmc runs (FETCH_SIZE, WRITE_SIZE) made with --copy-calibration")
     return p.parse_args()
+
+
+def ffn_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in FFN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per expert-FFN call from the PMC runs kept in profiles/, or None
+    when there are none for this workload or the FFN sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            entry = json.load(fh).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not entry or entry.get("ffn_source_sha256") != ffn_source_digest():
+        return None
+    return entry
+
+
+def _pmc_means(csv_dir: str, counter: str):
+    """Per kernel name: mean of `counter` over its dispatches; also the largest
+    value among the runtime's copy kernels (the calibration copy)."""
+    sums, counts, copy_max = {}, {}, 0.0
+    with open(os.path.join(csv_dir, "run_counter_collection.csv")) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            v, name = float(r["Counter_Value"]), r["Kernel_Name"]
+            if "rocclr_copyBuffer" in name:
+                copy_max = max(copy_max, v)
+            sums[name] = sums.get(name, 0.0) + v
+            counts[name] = counts.get(name, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}, copy_max
+
+
+def summarize_traffic(args):
+    from sparse_moe_amd import synth
+    fetch_dir, write_dir, calib_mib, cmd = args.summarize_traffic
+    calib = float(calib_mib) * 1024  # KiB
+    spec = synth.SPECS[args.config]
+    out = {}
+    for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        means, copy_kib = _pmc_means(d, counter)
+        if copy_kib <= 0:
+            sys.exit("no calibration copy found in %s" % d)
+        scale = calib / copy_kib
+        ffn = {k: v for k, v in means.items() if "ffn_gemv_q4_0" in k or "ffn_mfma" in k}
+        out[key + "_bytes"] = sum(ffn.values()) * 1024 * scale
+        out[key + "_scale"] = scale
+        out[key + "_kib_per_kernel"] = {
+            k.replace("(anonymous namespace)::", "").split("(")[0]: v for k, v in ffn.items()}
+    out["traffic_bytes"] = out["fetch_bytes"] + out["write_bytes"]
+    out["ffn_source_sha256"] = ffn_source_digest()
+    out["commands"] = cmd
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            allw = json.load(fh)
+    except (OSError, ValueError):
+        allw = {}
+    allw[spec.name] = out
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(allw, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps({spec.name: out}))
+
+
+def summarize_stats(args):
+    csv_dir, out_md, title, cmd = args.summarize_stats
+    with open(os.path.join(csv_dir, "run_kernel_stats.csv")) as fh:
+        rows = list(csv.DictReader(fh))
+    with open(out_md, "w") as f:
+        f.write("# %s\n\n" % title)
+        f.write("Command (from the repository root on one MI355X, rocprofv3 of ROCm 7.2):\n\n"
+                "```\n%s\n```\n\n" % cmd)
+        f.write("Calls include the warm-up, the eager passes and the graph replays; the torch "
+                "kernels are bench set-up.\n\n")
+        f.write("| kernel | calls | avg (us) | min (us) | max (us) | share of GPU time |\n"
+                "|---|---|---|---|---|---|\n")
+        for r in rows[:14]:
+            name = r["Name"].replace("|", "\\|")
+            if len(name) > 110:
+                name = name[:107] + "..."
+            f.write("| `%s` | %s | %.2f | %.2f | %.2f | %.1f%% |\n" % (
+                name, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    print("wrote", out_md)
 
 
 def cpu_baseline(spec, seconds: float):
@@ -229,6 +336,10 @@ def cpu_baseline_stack(spec, seconds: float):
 
 def main():
     args = parse()
+    if args.summarize_stats:
+        return summarize_stats(args)
+    if args.summarize_traffic:
+        return summarize_traffic(args)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see DESIGN.md for how the layer would shard over experts)", file=sys.stderr)
@@ -236,6 +347,13 @@ def main():
     import torch
     from sparse_moe_amd import binding, synth
     torch.cuda.set_device(0)
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     spec = synth.SPECS[args.config]
     if spec.layers > 1:
         return bench_stack(args, spec)
@@ -354,6 +472,11 @@ def main():
                     "bytes_per_launch": ffn_bytes, "avg_launch_us": ffn_avg_ms * 1e3}
         dtype = "q4_0 x %s (int4 digit products, fp32 accumulate)" % spec.act
     layer_tflops = ffn_flops / (ms_step * 1e-3) / 1e12
+    tr = stored_traffic(spec.name)
+    if tr is not None:
+        roofline["traffic"] = tr["traffic_bytes"]
+        roofline["traffic_fetch"] = tr["fetch_bytes"]
+        roofline["traffic_write"] = tr["write_bytes"]
 
     res = {
         "metric": METRIC,
