@@ -21,6 +21,8 @@
 // activation digits stay in registers; a row is covered by LPR lanes (a power
 // of two >= blocks/2), a wave covers 64/LPR rows per step, and the loads of a
 // wave are contiguous.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace moe {
@@ -129,6 +131,19 @@ MOE_DEV PairDec lds_pair(const uint8_t* p, int nh) {
     return d;
 }
 
+// the same window already in registers (rows of an even block count)
+MOE_DEV PairDec reg_pair(const uint32_t (&w)[9], int nh) {
+    PairDec d;
+    d.dA = nh >= 1 ? f16_bits_to_f32(w[0]) : 0.f;
+    d.dB = nh == 2 ? f16_bits_to_f32(w[4] >> 16) : 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        d.qA[m] = __builtin_amdgcn_perm(w[m + 1], w[m], 0x05040302u);
+        d.qB[m] = w[5 + m];
+    }
+    return d;
+}
+
 // Load bytes [s0, s1) of a weight matrix with coalesced 16-byte loads
 // (consecutive lanes read consecutive 16 bytes) into registers; store_span then
 // writes them to the wave's LDS region.  The copy starts at the 16-byte boundary
@@ -171,7 +186,13 @@ constexpr int steps_per_wave() {
 // pair q of row g from LDS.  Tokens of the expert are processed in chunks of TC
 // whose activation digits are staged in LDS once per workgroup.
 // One workgroup tile: rows [bx * 4 * RPW, ...) of the by-th active expert.
-template <int MODE, int ADT, int LPR, int TC, int UPW, bool EVEN_NB>
+// DIRECT (rows of an even block count only): every lane loads its own 36-byte
+// pair windows straight into registers (two 16-byte and one 4-byte load per
+// window) instead of staging the rows through LDS with coalesced loads.  The
+// requests are less regular, but the workgroup needs no LDS for weights, so
+// more workgroups fit on a CU and more of the stream is in flight: the better
+// trade when the grid is several times the chip (many experts, few tokens).
+template <int MODE, int ADT, int LPR, int TC, int UPW, bool EVEN_NB, bool DIRECT>
 MOE_DEV void gemv_tile(const uint8_t* __restrict__ W, int nb, int I, int H,
                        const void* __restrict__ act, const int32_t* __restrict__ offsets,
                        const int32_t* __restrict__ sorted_slots, int K, int E,
@@ -273,13 +294,37 @@ MOE_DEV void gemv_tile(const uint8_t* __restrict__ W, int nb, int I, int H,
     load_x(0);  // first: so that waiting for the activations does not wait for the weights
 
     // -- this wave's rows: all loads in flight at once (into registers)
+    constexpr int NCHS = DIRECT ? 1 : NCH;
+    constexpr int UD = DIRECT ? UPW : 1, ND = DIRECT ? NR : 1;
     int loff[NR];
-    u32x4a4 wreg[NR][NCH];
+    u32x4a4 wreg[NR][NCHS];
+    uint32_t wd[UD][ND][9];
+    if constexpr (DIRECT) {
+        // unconditional (clamped to a valid row and pair) so that the number of
+        // loads in flight is static
+        const int qq = min(q, nb / 2 - 1);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {  // unconditional: waves past the last row load one chunk
-        const int64_t s0 = nrows > 0 ? (int64_t)(row0 + r * I) * row_bytes : 0;
-        const int64_t s1 = nrows > 0 ? s0 + nrows * row_bytes : 16;
-        loff[r] = load_span<NCH>(We, s0, s1, lane, wreg[r]);
+        for (int u = 0; u < UPW; ++u) {
+            const int lr = min(u * RPS + g, max(nrows - 1, 0));
+            const int row = nrows > 0 ? row0 + lr : 0;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const uint8_t* p = We + (int64_t)(row + r * I) * row_bytes + 36 * qq;
+                const u32x4a4 a = *reinterpret_cast<const u32x4a4*>(p);
+                const u32x4a4 b = *reinterpret_cast<const u32x4a4*>(p + 16);
+                const uint32_t c = *reinterpret_cast<const uint32_t*>(p + 32);
+                wd[u][r][0] = a.x; wd[u][r][1] = a.y; wd[u][r][2] = a.z; wd[u][r][3] = a.w;
+                wd[u][r][4] = b.x; wd[u][r][5] = b.y; wd[u][r][6] = b.z; wd[u][r][7] = b.w;
+                wd[u][r][8] = c;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {  // unconditional: waves past the last row load one chunk
+            const int64_t s0 = nrows > 0 ? (int64_t)(row0 + r * I) * row_bytes : 0;
+            const int64_t s1 = nrows > 0 ? s0 + nrows * row_bytes : 16;
+            loff[r] = load_span<NCHS>(We, s0, s1, lane, wreg[r]);
+        }
     }
     if (nbp != nb) {  // the pad block of an odd block count reads as zero
         for (int i = tid; i < TC * 16; i += 256) dig[i * nbp + nb] = 0u;
@@ -288,9 +333,9 @@ MOE_DEV void gemv_tile(const uint8_t* __restrict__ W, int nb, int I, int H,
 
     // products of the staged rows with the chunk's digits, reductions, outputs
     auto compute = [&](int c0) {
-        if (c0 == 0) {
+        if (!DIRECT && c0 == 0) {
 #pragma unroll
-            for (int r = 0; r < NR; ++r) store_span<NCH>(wl + r * (span_bytes + 16), lane, wreg[r]);
+            for (int r = 0; r < NR; ++r) store_span<NCHS>(wl + r * (span_bytes + 16), lane, wreg[r]);
         }
         __syncthreads();  // digits of every wave and this wave's rows are in LDS
         const int qp = min(q, nbp / 2 - 1);   // lanes past the row's pairs read a valid pair
@@ -316,8 +361,13 @@ MOE_DEV void gemv_tile(const uint8_t* __restrict__ W, int nb, int I, int H,
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
                 const int nh = lr < nrows ? nblk_here : 0;
-                const int off = loff[r] + lr * (int)row_bytes + 36 * q;
-                const PairDec w = lds_pair<EVEN_NB>(wl + r * (span_bytes + 16) + (nh > 0 ? off : 0), nh);
+                PairDec w;
+                if constexpr (DIRECT) {
+                    w = reg_pair(wd[u][r], nh);
+                } else {
+                    const int off = loff[r] + lr * (int)row_bytes + 36 * q;
+                    w = lds_pair<EVEN_NB>(wl + r * (span_bytes + 16) + (nh > 0 ? off : 0), nh);
+                }
 #pragma unroll
                 for (int t = 0; t < TC; ++t) {
                     const int ia = block_idot(w.qA, xa[t]);
@@ -383,18 +433,18 @@ MOE_DEV void gemv_tile(const uint8_t* __restrict__ W, int nb, int I, int H,
     }
 }
 
-template <int MODE, int ADT, int LPR, int TC, int UPW, bool EVEN_NB>
+template <int MODE, int ADT, int LPR, int TC, int UPW, bool EVEN_NB, bool DIRECT>
 __global__ __launch_bounds__(256) void ffn_gemv_q4_0(
     const uint8_t* __restrict__ W, int nb, int I, int H, const void* __restrict__ act,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slots, int K, int E,
     void* __restrict__ out, int wave_lds_bytes) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    gemv_tile<MODE, ADT, LPR, TC, UPW, EVEN_NB>(W, nb, I, H, act, offsets, sorted_slots, K, E, out,
+    gemv_tile<MODE, ADT, LPR, TC, UPW, EVEN_NB, DIRECT>(W, nb, I, H, act, offsets, sorted_slots, K, E, out,
                                                 wave_lds_bytes, smem, blockIdx.x, blockIdx.y);
 }
 
 // ---- dispatch ---------------------------------------------------------------------
-template <int MODE, int ADT, int LPR, int TC, bool EVEN_NB>
+template <int MODE, int ADT, int LPR, int TC, bool EVEN_NB, bool DIRECT>
 static void launch_mode(const uint8_t* W, int nb, int I, int H, const void* act,
                         const int32_t* offsets, const int32_t* sorted_slots, int K, int E,
                         int n_active, void* out, hipStream_t st) {
@@ -405,14 +455,14 @@ static void launch_mode(const uint8_t* W, int nb, int I, int H, const void* act,
     const int rows_out = (MODE == 0) ? I : H;
     const int wgs = (rows_out + 4 * RPW - 1) / (4 * RPW);
     constexpr int NCH = (RPW * 36 * LPR + 15 + 1023) / 1024;
-    const int wave_lds = NR * NCH * 1024;
+    const int wave_lds = DIRECT ? 0 : NR * NCH * 1024;
     const size_t lds = (size_t)4 * wave_lds + (size_t)TC * ((nb + 1) & ~1) * 17 * sizeof(uint32_t);
     dim3 grid(wgs, n_active);
-    ffn_gemv_q4_0<MODE, ADT, LPR, TC, UPW, EVEN_NB><<<grid, 256, lds, st>>>(
+    ffn_gemv_q4_0<MODE, ADT, LPR, TC, UPW, EVEN_NB, DIRECT><<<grid, 256, lds, st>>>(
         W, nb, I, H, act, offsets, sorted_slots, K, E, out, wave_lds);
 }
 
-template <int MODE, int ADT, int TC>
+template <int MODE, int ADT, int TC, bool DIRECT>
 static void launch_lpr(const uint8_t* W, int nb, int I, int H, const void* act,
                        const int32_t* offsets, const int32_t* sorted_slots, int K, int E,
                        int n_active, void* out, hipStream_t st) {
@@ -420,11 +470,12 @@ static void launch_lpr(const uint8_t* W, int nb, int I, int H, const void* act,
 #define MOE_LPR_CASE(L)                                                                         \
     if (pairs <= L) {                                                                           \
         if (nb & 1)                                                                             \
-            launch_mode<MODE, ADT, L, TC, false>(W, nb, I, H, act, offsets, sorted_slots, K, E, \
-                                                 n_active, out, st);                            \
+            launch_mode<MODE, ADT, L, TC, false, false>(W, nb, I, H, act, offsets, sorted_slots, K, \
+                                                        E, n_active, out, st);                  \
         else                                                                                    \
-            launch_mode<MODE, ADT, L, TC, true>(W, nb, I, H, act, offsets, sorted_slots, K, E,  \
-                                                n_active, out, st);                             \
+            launch_mode<MODE, ADT, L, TC, true, DIRECT>(W, nb, I, H, act, offsets,              \
+                                                              sorted_slots, K, E, n_active, out,  \
+                                                              st);                                \
         return;                                                                                 \
     }
     MOE_LPR_CASE(1) MOE_LPR_CASE(2) MOE_LPR_CASE(4) MOE_LPR_CASE(8) MOE_LPR_CASE(16)
@@ -432,13 +483,13 @@ static void launch_lpr(const uint8_t* W, int nb, int I, int H, const void* act,
 #undef MOE_LPR_CASE
 }
 
-template <int ADT, int TC>
+template <int ADT, int TC, bool DIRECT>
 static void launch_both(const void* x, int H, const uint8_t* w_gate_up, const uint8_t* w_down,
                         int I, int E, int K, int n_active, const int32_t* offsets,
                         const int32_t* sorted_slots, void* h_ws, float* y_sorted, hipStream_t st) {
-    launch_lpr<0, ADT, TC>(w_gate_up, H / 32, I, H, x, offsets, sorted_slots, K, E, n_active, h_ws,
+    launch_lpr<0, ADT, TC, DIRECT>(w_gate_up, H / 32, I, H, x, offsets, sorted_slots, K, E, n_active, h_ws,
                            st);
-    launch_lpr<1, ADT, TC>(w_down, I / 32, I, H, h_ws, offsets, sorted_slots, K, E, n_active,
+    launch_lpr<1, ADT, TC, DIRECT>(w_down, I / 32, I, H, h_ws, offsets, sorted_slots, K, E, n_active,
                            y_sorted, st);
 }
 
@@ -447,22 +498,28 @@ hipError_t launch_ffn_gemv(const void* x, int x_dt, int64_t T, int H, const uint
                            const int32_t* offsets, const int32_t* sorted_slots, void* h_ws,
                            float* y_sorted, hipStream_t st) {
     const int n_active = min(E, N);
-    // tokens per expert never exceed T: one token per chunk when T == 1
-    if (x_dt == MOE_F32) {
-        if (T == 1)
-            launch_both<MOE_F32, 1>(x, H, w_gate_up, w_down, I, E, K, n_active, offsets,
-                                    sorted_slots, h_ws, y_sorted, st);
-        else
-            launch_both<MOE_F32, 2>(x, H, w_gate_up, w_down, I, E, K, n_active, offsets,
-                                    sorted_slots, h_ws, y_sorted, st);
-    } else {
-        if (T == 1)
-            launch_both<MOE_BF16, 1>(x, H, w_gate_up, w_down, I, E, K, n_active, offsets,
-                                     sorted_slots, h_ws, y_sorted, st);
-        else
-            launch_both<MOE_BF16, 2>(x, H, w_gate_up, w_down, I, E, K, n_active, offsets,
-                                     sorted_slots, h_ws, y_sorted, st);
-    }
+    // One token: one chunk per expert, rows staged through LDS with coalesced
+    // loads (the grid is about one wave of workgroups, so the regular stream
+    // matters most).  Several tokens: direct register windows (twice the
+    // workgroups per CU), one token per chunk while experts average at most one
+    // slot, else two.
+    auto go = [&](auto adt, auto tc, auto direct) {
+        launch_both<decltype(adt)::value, decltype(tc)::value, decltype(direct)::value>(
+            x, H, w_gate_up, w_down, I, E, K, n_active, offsets, sorted_slots, h_ws, y_sorted, st);
+    };
+    using F32 = std::integral_constant<int, MOE_F32>;
+    using BF16 = std::integral_constant<int, MOE_BF16>;
+    using One = std::integral_constant<int, 1>;
+    using Two = std::integral_constant<int, 2>;
+    using Staged = std::false_type;
+    using Direct = std::true_type;
+    const bool f32 = x_dt == MOE_F32;
+    if (T == 1)
+        f32 ? go(F32{}, One{}, Staged{}) : go(BF16{}, One{}, Staged{});
+    else if ((int64_t)N <= E)
+        f32 ? go(F32{}, One{}, Direct{}) : go(BF16{}, One{}, Direct{});
+    else
+        f32 ? go(F32{}, Two{}, Direct{}) : go(BF16{}, Two{}, Direct{});
     return hipGetLastError();
 }
 
