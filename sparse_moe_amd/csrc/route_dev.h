@@ -106,16 +106,23 @@ MOE_DEV void permute_block(const int32_t* ids, int N, int E, int32_t* offsets,
 // logits.  Every lane of the wave must be active.
 // COH: the logits were written by other workgroups of this launch (coherent loads).
 template <bool COH = false>
-MOE_DEV void topk_token(const float* l, int E, int K, int32_t* ids, float* w) {
+MOE_DEV void topk_load(const float* l, int E, float (&v)[4]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? (COH ? coherent_load(l + e) : l[e]) : 0.f;
+    }
+}
+
+MOE_DEV void topk_select(const float (&lv)[4], int E, int K, int32_t* ids, float* w) {
     const int lane = threadIdx.x & 63;
     float v[4];
     bool live[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int e = lane + 64 * i;
-        live[i] = e < E;
-        const float le = live[i] ? (COH ? coherent_load(l + e) : l[e]) : 0.f;
-        v[i] = live[i] ? le + 0.f : -INFINITY;  // + 0 turns -0 into +0
+        live[i] = lane + 64 * i < E;
+        v[i] = live[i] ? lv[i] + 0.f : -INFINITY;  // + 0 turns -0 into +0
     }
     float selv[MOE_MAX_K];
     int seli[MOE_MAX_K];
@@ -161,6 +168,13 @@ MOE_DEV void topk_token(const float* l, int E, int K, int32_t* ids, float* w) {
         ids[lane] = myi;
         w[lane] = expf(myv - selv[0]) / s;
     }
+}
+
+template <bool COH = false>
+MOE_DEV void topk_token(const float* l, int E, int K, int32_t* ids, float* w) {
+    float v[4];
+    topk_load<COH>(l, E, v);
+    topk_select(v, E, K, ids, w);
 }
 
 }  // namespace moe

@@ -4,6 +4,8 @@
 // v3 artifact", table "What is inside": the router and router scale are FP32.
 // Each token keeps the K largest logits (descending; equal logits in ascending
 // expert order) with softmax weights over the K kept logits.
+#include <type_traits>
+
 #include "route_dev.h"
 
 namespace moe {
@@ -21,9 +23,12 @@ MOE_DEV float4 load_x4(const void* x, int xdt, int64_t i4) {
 }
 
 // One expert per workgroup: wave w takes a quarter of the float4 chunks of the
-// expert's W_r row, dots them with every token (all loads issued before the
-// reductions) and leaves its per-token partial sums in part[w][t].
-template <int XDT>
+// expert's W_r row, dots them with every token and leaves its per-token partial
+// sums in part[w][t].  Every load (W_r, router scale, the TT token rows) is
+// issued before the first product: the loads are unconditional, at clamped
+// chunk and token indices, so they go out together instead of one round trip
+// each.  Each token's products and sums are the same for any TT >= T.
+template <int XDT, int TT, bool RSC>
 MOE_DEV void expert_partials(const void* __restrict__ x, int T, int H, const float* __restrict__ W,
                              const float* __restrict__ rsc, int e,
                              float (*part)[ROUTER_GEMV_MAX_T]) {
@@ -32,33 +37,52 @@ MOE_DEV void expert_partials(const void* __restrict__ x, int T, int H, const flo
     const int c0 = wave * nch / 4, c1 = (wave + 1) * nch / 4;
     const float4* wr = reinterpret_cast<const float4*>(W + (int64_t)e * H);
     constexpr int CPW = ROUTER_MAX_CHUNKS / 4;
+    int j4[CPW];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        const int c = max(0, min(c0 + i, c1 - 1));  // a valid chunk even past this wave's range
+        j4[i] = min(lane + 64 * c, H4 - 1);
+    }
     float4 wv[CPW];
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-        const int c = c0 + i;
-        wv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (c < c1) {
-            const int j4 = min(lane + 64 * c, H4 - 1);
-            wv[i] = wr[j4];
-            if (rsc) {
-                const float4 sv = reinterpret_cast<const float4*>(rsc)[j4];
-                wv[i].x *= sv.x; wv[i].y *= sv.y; wv[i].z *= sv.z; wv[i].w *= sv.w;
-            }
-            if (lane + 64 * c >= H4) wv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+    for (int i = 0; i < CPW; ++i) wv[i] = wr[j4[i]];
+    float4 sv[RSC ? CPW : 1];
+    if constexpr (RSC) {
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) sv[i] = reinterpret_cast<const float4*>(rsc)[j4[i]];
     }
-    float acc[ROUTER_GEMV_MAX_T];
+    using XV = typename std::conditional<XDT == MOE_F32, float4, uint2>::type;
+    XV xr[CPW][TT];
 #pragma unroll
-    for (int t = 0; t < ROUTER_GEMV_MAX_T; ++t) acc[t] = 0.f;
+    for (int i = 0; i < CPW; ++i)
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+            xr[i][t] = reinterpret_cast<const XV*>(x)[(int64_t)min(t, T - 1) * H4 + j4[i]];
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
         const int c = c0 + i;
-        if (c < c1) {
-            const int j4 = min(lane + 64 * c, H4 - 1);
+        if (RSC) {
+            wv[i].x *= sv[i].x; wv[i].y *= sv[i].y; wv[i].z *= sv[i].z; wv[i].w *= sv[i].w;
+        }
+        if (c >= c1 || lane + 64 * c >= H4) wv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float acc[TT];
 #pragma unroll
-            for (int t = 0; t < ROUTER_GEMV_MAX_T; ++t) {
+    for (int t = 0; t < TT; ++t) acc[t] = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        if (c0 + i < c1) {
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
                 if (t < T) {
-                    const float4 xv = load_x4(x, XDT, (int64_t)t * H4 + j4);
+                    float4 xv;
+                    if constexpr (XDT == MOE_F32) {
+                        xv = xr[i][t];
+                    } else {
+                        const uint2 b = xr[i][t];
+                        xv = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
+                                         __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
+                    }
                     acc[t] = fmaf(xv.x, wv[i].x, acc[t]);
                     acc[t] = fmaf(xv.y, wv[i].y, acc[t]);
                     acc[t] = fmaf(xv.z, wv[i].z, acc[t]);
@@ -67,9 +91,12 @@ MOE_DEV void expert_partials(const void* __restrict__ x, int T, int H, const flo
             }
         }
     }
-    for (int t = 0; t < T; ++t) {
-        const float sum = wave_sum(acc[t]);
-        if (lane == 0) part[wave][t] = sum;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        if (t < T) {
+            const float sum = wave_sum(acc[t]);
+            if (lane == 0) part[wave][t] = sum;
+        }
     }
 }
 
@@ -77,7 +104,7 @@ MOE_DEV void expert_partials(const void* __restrict__ x, int T, int H, const flo
 // sequence of operations whatever T is and wherever the token sits in the batch
 // (the fused few-token kernel uses the same expert_partials and final sum), so
 // every T below ROUTER_MFMA_MIN_T routes a token exactly as T = 1 does.
-template <int XDT>
+template <int XDT, int TT, bool RSC>
 __global__ __launch_bounds__(256) void router_logits_gemv(const void* __restrict__ x, int T, int H,
                                                           const float* __restrict__ W,
                                                           const float* __restrict__ rsc,
@@ -88,7 +115,7 @@ __global__ __launch_bounds__(256) void router_logits_gemv(const void* __restrict
     const int t0 = blockIdx.y * ROUTER_GEMV_MAX_T, tg = min(ROUTER_GEMV_MAX_T, T - t0);
     const void* xg = XDT == MOE_F32 ? (const void*)((const float*)x + (int64_t)t0 * H)
                                     : (const void*)((const uint16_t*)x + (int64_t)t0 * H);
-    expert_partials<XDT>(xg, tg, H, W, rsc, e, part);
+    expert_partials<XDT, TT, RSC>(xg, tg, H, W, rsc, e, part);
     __syncthreads();
     const int t = threadIdx.x;
     if (t < tg)
@@ -181,7 +208,7 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ lo
 // the last workgroup to finish (counted with an agent-scope atomic in the
 // workspace) runs top-K for every token on coherently loaded logits and the
 // permutation of the T*K slots, and resets the counter to zero.
-template <int XDT>
+template <int XDT, int TT, bool RSC>
 __global__ __launch_bounds__(256) void route_small(const void* __restrict__ x, int T, int H,
                                                    const float* __restrict__ W,
                                                    const float* __restrict__ rsc,
@@ -195,7 +222,7 @@ __global__ __launch_bounds__(256) void route_small(const void* __restrict__ x, i
     const int wave = threadIdx.x >> 6;
     __shared__ float part[4][ROUTER_GEMV_MAX_T];
     const int e = blockIdx.x;  // one expert per workgroup, H split over its waves
-    expert_partials<XDT>(x, T, H, W, rsc, e, part);
+    expert_partials<XDT, TT, RSC>(x, T, H, W, rsc, e, part);
     __syncthreads();
     {
         const int t = threadIdx.x;
@@ -213,24 +240,46 @@ __global__ __launch_bounds__(256) void route_small(const void* __restrict__ x, i
     }
     __syncthreads();
     if (!s_last) return;
-    for (int t = wave; t < T; t += 4)
-        topk_token<true>(logits + (int64_t)t * E, E, K, ids + t * K, w + t * K);
+    // wave w takes tokens w and w + 4: both tokens' logits are loaded first
+    float v0[4], v1[4];
+    const int t0 = wave, t1 = wave + 4;
+    if (t0 < T) topk_load<true>(logits + (int64_t)t0 * E, E, v0);
+    if (t1 < T) topk_load<true>(logits + (int64_t)t1 * E, E, v1);
+    if (t0 < T) topk_select(v0, E, K, ids + t0 * K, w + t0 * K);
+    if (t1 < T) topk_select(v1, E, K, ids + t1 * K, w + t1 * K);
     __syncthreads();  // ids of every token are written
     permute_block(ids, T * K, E, offsets, sorted_slots, slot_pos);
     if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// token-count bucket (1, 2, 4 or 8 rows loaded per chunk) and router-scale
+// presence, as template arguments
+template <class F>
+static void router_variant(int x_dt, int T, bool rsc, F&& f) {
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I4 = std::integral_constant<int, 4>;
+    using I8 = std::integral_constant<int, 8>;
+    auto with_t = [&](auto xdt, auto r) {
+        if (T <= 1) f(xdt, I1{}, r);
+        else if (T <= 2) f(xdt, I2{}, r);
+        else if (T <= 4) f(xdt, I4{}, r);
+        else f(xdt, I8{}, r);
+    };
+    auto with_r = [&](auto xdt) { rsc ? with_t(xdt, std::true_type{}) : with_t(xdt, std::false_type{}); };
+    if (x_dt == MOE_F32) with_r(std::integral_constant<int, MOE_F32>{});
+    else with_r(std::integral_constant<int, MOE_BF16>{});
 }
 
 hipError_t launch_route_small(const void* x, int x_dt, int T, int H, const float* W,
                               const float* rsc, const float* bias, int E, int K, float* logits,
                               int32_t* ids, float* w, int32_t* offsets, int32_t* sorted_slots,
                               int32_t* slot_pos, int* counter, hipStream_t st) {
-    dim3 grid(E);
-    if (x_dt == MOE_F32)
-        route_small<MOE_F32><<<grid, 256, 0, st>>>(x, T, H, W, rsc, bias, E, K, logits, ids, w,
-                                                   offsets, sorted_slots, slot_pos, counter);
-    else
-        route_small<MOE_BF16><<<grid, 256, 0, st>>>(x, T, H, W, rsc, bias, E, K, logits, ids, w,
-                                                    offsets, sorted_slots, slot_pos, counter);
+    router_variant(x_dt, T, rsc != nullptr, [&](auto xdt, auto tt, auto r) {
+        route_small<decltype(xdt)::value, decltype(tt)::value, decltype(r)::value>
+            <<<dim3(E), 256, 0, st>>>(x, T, H, W, rsc, bias, E, K, logits, ids, w, offsets,
+                                      sorted_slots, slot_pos, counter);
+    });
     return hipGetLastError();
 }
 
@@ -383,10 +432,10 @@ hipError_t launch_router_logits(const void* x, int x_dt, int64_t T, int H, const
                                                  logits);
     } else if (T < ROUTER_MFMA_MIN_T) {
         dim3 grid(E, (unsigned)((T + ROUTER_GEMV_MAX_T - 1) / ROUTER_GEMV_MAX_T));
-        if (x_dt == MOE_F32)
-            router_logits_gemv<MOE_F32><<<grid, 256, 0, st>>>(x, (int)T, H, W, rsc, bias, E, logits);
-        else
-            router_logits_gemv<MOE_BF16><<<grid, 256, 0, st>>>(x, (int)T, H, W, rsc, bias, E, logits);
+        router_variant(x_dt, (int)T, rsc != nullptr, [&](auto xdt, auto tt, auto r) {
+            router_logits_gemv<decltype(xdt)::value, decltype(tt)::value, decltype(r)::value>
+                <<<grid, 256, 0, st>>>(x, (int)T, H, W, rsc, bias, E, logits);
+        });
     } else {
         dim3 grid((unsigned)((T + RT_BM - 1) / RT_BM), (E + RT_BN - 1) / RT_BN);
         if (x_dt == MOE_F32)

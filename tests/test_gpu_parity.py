@@ -83,6 +83,33 @@ def test_fused_route_repeated_calls_reset_the_counter():
     assert int(bufs.ws_route[:4].view(torch.int32).item()) == 0
 
 
+@pytest.mark.parametrize("E,K", [(128, 8), (100, 16), (256, 16), (8, 8), (65, 1)])
+def test_topk_exact_ties(E, K):
+    # Zero router weights make every logit equal its bias exactly; biases drawn
+    # from a few values (with -0 and +0) give many exact ties, which must resolve
+    # to the lower expert index (descending logit, then ascending index) in the
+    # fused few-token kernel and in the one-wave-per-token top-K kernel alike.
+    from sparse_moe_amd import binding
+    rng = np.random.default_rng(E * 31 + K)
+    H, T = 64, 3
+    bias = rng.choice(np.array([-1.5, -0.0, 0.0, 0.25, 2.0], np.float32), size=E)
+    x = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).cuda()
+    wr = torch.zeros((E, H), dtype=torch.float32, device="cuda")
+    b = torch.from_numpy(bias).cuda()
+    logits_ref = np.repeat(bias[None, :].astype(np.float64) + 0.0, T, axis=0)
+    ids_ref, w_ref = oracle.topk_softmax(logits_ref, K)
+    for fused in (True, False):
+        bufs = binding.LayerBuffers(T, H, 64, E, K, torch.float32)
+        if fused:
+            binding.moe_route(x, wr, bufs.logits, bufs.topk_ids, bufs.topk_w, bufs.offsets,
+                              bufs.sorted_slots, bufs.slot_pos, bufs.ws_route, logit_bias=b)
+        else:
+            binding.moe_router_topk(x, wr, bufs.logits, bufs.topk_ids, bufs.topk_w, logit_bias=b)
+        torch.cuda.synchronize()
+        assert np.array_equal(bufs.topk_ids.cpu().numpy(), ids_ref), (fused, E, K)
+        assert np.max(np.abs(bufs.topk_w.cpu().numpy() - w_ref)) <= 1e-6
+
+
 def test_odd_block_count_rows():
     # H = 32 * 9 and I = 32 * 3: rows with an odd number of Q4_0 blocks
     spec = synth.LayerSpec("odd-blocks", H=288, E=8, K=2, I=96, T=5, act="f32",
