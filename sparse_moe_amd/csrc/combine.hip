@@ -8,8 +8,11 @@
 namespace moe {
 
 // out[t, o] = sum_k (w[t,k] * scale[e_k]) * y[slot_pos[t*K+k], o], fixed k order.
-// One workgroup per token; each thread owns 4 consecutive outputs per step.
-template <int RDT, int ODT>
+// Workgroup (t, b): token t, outputs 4*(256*b + thread) .. +3.  The K weights,
+// scales and row positions are uniform loads; all K rows' loads are issued
+// before the first product (KB >= K rows, clamped to a valid k), so a
+// workgroup costs two dependent memory round trips whatever K is.
+template <int RDT, int ODT, int KB>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const int32_t* __restrict__ slot_pos,
                                                       const int32_t* __restrict__ ids,
@@ -19,35 +22,40 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       float* __restrict__ out_f32,
                                                       void* __restrict__ out_act) {
     const int64_t t = blockIdx.x;
-    __shared__ float c[MOE_MAX_K];
-    __shared__ int pos[MOE_MAX_K];
-    if (threadIdx.x < K) {
-        const int64_t s = t * K + threadIdx.x;
-        c[threadIdx.x] = w[s] * (scale ? scale[ids[s]] : 1.f);
-        pos[threadIdx.x] = slot_pos[s];
-    }
-    __syncthreads();
     const int H4 = H >> 2;
-    for (int j4 = threadIdx.x; j4 < H4; j4 += blockDim.x) {
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int k = 0; k < K; ++k) {
-            const float4 v = reinterpret_cast<const float4*>(y + (int64_t)pos[k] * H)[j4];
-            acc.x = fmaf(c[k], v.x, acc.x);
-            acc.y = fmaf(c[k], v.y, acc.y);
-            acc.z = fmaf(c[k], v.z, acc.z);
-            acc.w = fmaf(c[k], v.w, acc.w);
-        }
-        const int64_t o = t * H + 4 * j4;
-        if (out_f32) *reinterpret_cast<float4*>(out_f32 + o) = acc;
-        if (out_act) {
-            float r[4] = {acc.x, acc.y, acc.z, acc.w};
-            if (residual) {
+    const int j4 = min((int)(blockIdx.y * blockDim.x + threadIdx.x), H4 - 1);
+    float c[KB];
+    int64_t row[KB];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) r[i] += load_act(residual, RDT, o + i);
-            }
+    for (int k = 0; k < KB; ++k) {
+        const int64_t s = t * K + min(k, K - 1);
+        c[k] = w[s] * (scale ? scale[ids[s]] : 1.f);
+        row[k] = (int64_t)slot_pos[s] * H4;
+    }
+    float4 v[KB];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) store_act(out_act, ODT, o + i, r[i]);
+    for (int k = 0; k < KB; ++k) v[k] = reinterpret_cast<const float4*>(y)[row[k] + j4];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+        if (k < K) {
+            acc.x = fmaf(c[k], v[k].x, acc.x);
+            acc.y = fmaf(c[k], v[k].y, acc.y);
+            acc.z = fmaf(c[k], v[k].z, acc.z);
+            acc.w = fmaf(c[k], v[k].w, acc.w);
         }
+    }
+    if ((int)(blockIdx.y * blockDim.x + threadIdx.x) >= H4) return;
+    const int64_t o = t * H + 4 * j4;
+    if (out_f32) *reinterpret_cast<float4*>(out_f32 + o) = acc;
+    if (out_act) {
+        float r[4] = {acc.x, acc.y, acc.z, acc.w};
+        if (residual) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r[i] += load_act(residual, RDT, o + i);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store_act(out_act, ODT, o + i, r[i]);
     }
 }
 
@@ -55,10 +63,13 @@ hipError_t launch_combine(const float* y, const int32_t* slot_pos, const int32_t
                           const float* w, const float* scale, int64_t T, int K, int H,
                           const void* residual, int rdt, float* out_f32, void* out_act, int odt,
                           hipStream_t st) {
-    dim3 grid((unsigned)T);
     const int threads = H >= 1024 ? 256 : 64;
-#define MOE_COMB(R, O) \
-    combine_kernel<R, O><<<grid, threads, 0, st>>>(y, slot_pos, ids, w, scale, K, H, residual, out_f32, out_act)
+    dim3 grid((unsigned)T, (unsigned)((H / 4 + threads - 1) / threads));
+#define MOE_COMB(R, O)                                                                          \
+    (K <= 8 ? combine_kernel<R, O, 8><<<grid, threads, 0, st>>>(y, slot_pos, ids, w, scale, K, H, \
+                                                                residual, out_f32, out_act)     \
+            : combine_kernel<R, O, MOE_MAX_K><<<grid, threads, 0, st>>>(                        \
+                  y, slot_pos, ids, w, scale, K, H, residual, out_f32, out_act))
     if (rdt == MOE_F32 && odt == MOE_F32) MOE_COMB(MOE_F32, MOE_F32);
     else if (rdt == MOE_F32) MOE_COMB(MOE_F32, MOE_BF16);
     else if (odt == MOE_F32) MOE_COMB(MOE_BF16, MOE_F32);
