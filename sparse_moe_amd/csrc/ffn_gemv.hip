@@ -192,7 +192,9 @@ constexpr int steps_per_wave() {
 // requests are less regular, but the workgroup needs no LDS for weights, so
 // more workgroups fit on a CU and more of the stream is in flight: the better
 // trade when the grid is several times the chip (many experts, few tokens).
-template <int MODE, int ADT, int LPR, int TC, int UPW, bool EVEN_NB, bool DIRECT>
+// ONE: a single-token call, so every gate/up slot reads activation row 0 (no
+// dependent read of the slot's token before the activation loads).
+template <int MODE, int ADT, int LPR, int TC, int UPW, bool EVEN_NB, bool DIRECT, bool ONE>
 MOE_DEV void gemv_tile(const uint8_t* __restrict__ W, int nb, int I, int H,
                        const void* __restrict__ act, const int32_t* __restrict__ offsets,
                        const int32_t* __restrict__ sorted_slots, int K, int E,
@@ -255,7 +257,7 @@ MOE_DEV void gemv_tile(const uint8_t* __restrict__ W, int nb, int I, int H,
 #pragma unroll
         for (int t = 0; t < TC; ++t) {
             const int p = __builtin_amdgcn_readfirstlane(p0 + min(c0 + t, ne_tok - 1));
-            src_row[t] = (MODE == 0) ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
+            src_row[t] = (MODE == 0) ? (ONE ? 0 : (int64_t)(sorted_slots[p] / K)) : (int64_t)p;
         }
 #pragma unroll
         for (int i = 0; i < NTASK; ++i) {
@@ -433,18 +435,18 @@ MOE_DEV void gemv_tile(const uint8_t* __restrict__ W, int nb, int I, int H,
     }
 }
 
-template <int MODE, int ADT, int LPR, int TC, int UPW, bool EVEN_NB, bool DIRECT>
+template <int MODE, int ADT, int LPR, int TC, int UPW, bool EVEN_NB, bool DIRECT, bool ONE>
 __global__ __launch_bounds__(256) void ffn_gemv_q4_0(
     const uint8_t* __restrict__ W, int nb, int I, int H, const void* __restrict__ act,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_slots, int K, int E,
     void* __restrict__ out, int wave_lds_bytes) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    gemv_tile<MODE, ADT, LPR, TC, UPW, EVEN_NB, DIRECT>(W, nb, I, H, act, offsets, sorted_slots, K, E, out,
+    gemv_tile<MODE, ADT, LPR, TC, UPW, EVEN_NB, DIRECT, ONE>(W, nb, I, H, act, offsets, sorted_slots, K, E, out,
                                                 wave_lds_bytes, smem, blockIdx.x, blockIdx.y);
 }
 
 // ---- dispatch ---------------------------------------------------------------------
-template <int MODE, int ADT, int LPR, int TC, bool EVEN_NB, bool DIRECT>
+template <int MODE, int ADT, int LPR, int TC, bool EVEN_NB, bool DIRECT, bool ONE>
 static void launch_mode(const uint8_t* W, int nb, int I, int H, const void* act,
                         const int32_t* offsets, const int32_t* sorted_slots, int K, int E,
                         int n_active, void* out, hipStream_t st) {
@@ -458,11 +460,11 @@ static void launch_mode(const uint8_t* W, int nb, int I, int H, const void* act,
     const int wave_lds = DIRECT ? 0 : NR * NCH * 1024;
     const size_t lds = (size_t)4 * wave_lds + (size_t)TC * ((nb + 1) & ~1) * 17 * sizeof(uint32_t);
     dim3 grid(wgs, n_active);
-    ffn_gemv_q4_0<MODE, ADT, LPR, TC, UPW, EVEN_NB, DIRECT><<<grid, 256, lds, st>>>(
+    ffn_gemv_q4_0<MODE, ADT, LPR, TC, UPW, EVEN_NB, DIRECT, ONE><<<grid, 256, lds, st>>>(
         W, nb, I, H, act, offsets, sorted_slots, K, E, out, wave_lds);
 }
 
-template <int MODE, int ADT, int TC, bool DIRECT>
+template <int MODE, int ADT, int TC, bool DIRECT, bool ONE>
 static void launch_lpr(const uint8_t* W, int nb, int I, int H, const void* act,
                        const int32_t* offsets, const int32_t* sorted_slots, int K, int E,
                        int n_active, void* out, hipStream_t st) {
@@ -470,10 +472,10 @@ static void launch_lpr(const uint8_t* W, int nb, int I, int H, const void* act,
 #define MOE_LPR_CASE(L)                                                                         \
     if (pairs <= L) {                                                                           \
         if (nb & 1)                                                                             \
-            launch_mode<MODE, ADT, L, TC, false, false>(W, nb, I, H, act, offsets, sorted_slots, K, \
+            launch_mode<MODE, ADT, L, TC, false, false, ONE>(W, nb, I, H, act, offsets, sorted_slots, K, \
                                                         E, n_active, out, st);                  \
         else                                                                                    \
-            launch_mode<MODE, ADT, L, TC, true, DIRECT>(W, nb, I, H, act, offsets,              \
+            launch_mode<MODE, ADT, L, TC, true, DIRECT, ONE>(W, nb, I, H, act, offsets,         \
                                                               sorted_slots, K, E, n_active, out,  \
                                                               st);                                \
         return;                                                                                 \
@@ -483,13 +485,13 @@ static void launch_lpr(const uint8_t* W, int nb, int I, int H, const void* act,
 #undef MOE_LPR_CASE
 }
 
-template <int ADT, int TC, bool DIRECT>
+template <int ADT, int TC, bool DIRECT, bool ONE>
 static void launch_both(const void* x, int H, const uint8_t* w_gate_up, const uint8_t* w_down,
                         int I, int E, int K, int n_active, const int32_t* offsets,
                         const int32_t* sorted_slots, void* h_ws, float* y_sorted, hipStream_t st) {
-    launch_lpr<0, ADT, TC, DIRECT>(w_gate_up, H / 32, I, H, x, offsets, sorted_slots, K, E, n_active, h_ws,
+    launch_lpr<0, ADT, TC, DIRECT, ONE>(w_gate_up, H / 32, I, H, x, offsets, sorted_slots, K, E, n_active, h_ws,
                            st);
-    launch_lpr<1, ADT, TC, DIRECT>(w_down, I / 32, I, H, h_ws, offsets, sorted_slots, K, E, n_active,
+    launch_lpr<1, ADT, TC, DIRECT, ONE>(w_down, I / 32, I, H, h_ws, offsets, sorted_slots, K, E, n_active,
                            y_sorted, st);
 }
 
@@ -503,9 +505,10 @@ hipError_t launch_ffn_gemv(const void* x, int x_dt, int64_t T, int H, const uint
     // matters most).  Several tokens: direct register windows (twice the
     // workgroups per CU), one token per chunk while experts average at most one
     // slot, else two.
-    auto go = [&](auto adt, auto tc, auto direct) {
-        launch_both<decltype(adt)::value, decltype(tc)::value, decltype(direct)::value>(
-            x, H, w_gate_up, w_down, I, E, K, n_active, offsets, sorted_slots, h_ws, y_sorted, st);
+    auto go = [&](auto adt, auto tc, auto direct, auto one) {
+        launch_both<decltype(adt)::value, decltype(tc)::value, decltype(direct)::value,
+                    decltype(one)::value>(x, H, w_gate_up, w_down, I, E, K, n_active, offsets,
+                                          sorted_slots, h_ws, y_sorted, st);
     };
     using F32 = std::integral_constant<int, MOE_F32>;
     using BF16 = std::integral_constant<int, MOE_BF16>;
@@ -513,13 +516,15 @@ hipError_t launch_ffn_gemv(const void* x, int x_dt, int64_t T, int H, const uint
     using Two = std::integral_constant<int, 2>;
     using Staged = std::false_type;
     using Direct = std::true_type;
+    using Single = std::true_type;
+    using Many = std::false_type;
     const bool f32 = x_dt == MOE_F32;
     if (T == 1)
-        f32 ? go(F32{}, One{}, Staged{}) : go(BF16{}, One{}, Staged{});
+        f32 ? go(F32{}, One{}, Staged{}, Single{}) : go(BF16{}, One{}, Staged{}, Single{});
     else if ((int64_t)N <= E)
-        f32 ? go(F32{}, One{}, Direct{}) : go(BF16{}, One{}, Direct{});
+        f32 ? go(F32{}, One{}, Direct{}, Many{}) : go(BF16{}, One{}, Direct{}, Many{});
     else
-        f32 ? go(F32{}, Two{}, Direct{}) : go(BF16{}, Two{}, Direct{});
+        f32 ? go(F32{}, Two{}, Direct{}, Many{}) : go(BF16{}, Two{}, Direct{}, Many{});
     return hipGetLastError();
 }
 
