@@ -56,12 +56,13 @@ def lib() -> C.CDLL:
         L.orc_permute.argtypes = [p, i64, i32, i32, p, p, p]
         L.orc_expert_ffn_token.argtypes = [p, i32, i32, p, p, i32, i32, p, p]
         L.orc_expert_ffn.argtypes = [p, i32, i64, i32, p, p, i32, i32, i32, p, p, p, p]
+        L.orc_linear_q4_0.argtypes = [p, i32, i64, i32, p, i32, p]
         L.orc_combine.argtypes = [p, p, p, p, p, i64, i32, i32, p, p]
         L.orc_rmsnorm.argtypes = [p, i32, p, d, i64, i32, p]
         L.orc_moe_layer.argtypes = [p, i32, i64, i32, p, p, p, p, i32, i32, p, p, i32, p, p,
                                     p, p, p, p, p, p, p]
         for f in ("orc_router_logits", "orc_topk_softmax", "orc_topk_weights", "orc_permute", "orc_expert_ffn_token",
-                  "orc_expert_ffn", "orc_combine", "orc_rmsnorm", "orc_moe_layer"):
+                  "orc_expert_ffn", "orc_linear_q4_0", "orc_combine", "orc_rmsnorm", "orc_moe_layer"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -167,6 +168,18 @@ def expert_ffn_token(x_row, w_gate_up, w_down, e: int):
                                       _ptr(w_down), I, e, _ptr(h), _ptr(y)),
            "orc_expert_ffn_token")
     return h, y
+
+
+def linear_q4_0(x, w) -> np.ndarray:
+    """y [T, R] = x [T, H] times the Q4_0 matrix w [R, H/32, 18] (transposed)."""
+    x = np.ascontiguousarray(x)
+    T, H = x.shape
+    w = np.ascontiguousarray(w, np.uint8)
+    R = w.shape[0]
+    assert w.shape[1] * 32 == H and w.shape[2] == 18
+    y = np.empty((T, R), np.float64)
+    _check(lib().orc_linear_q4_0(_ptr(x), _act(x), T, H, _ptr(w), R, _ptr(y)), "orc_linear_q4_0")
+    return y
 
 
 def expert_ffn(x, w_gate_up, w_down, K: int, offsets, sorted_slots, slot_mask=None):

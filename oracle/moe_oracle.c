@@ -212,6 +212,21 @@ int orc_expert_ffn_token(const void* x_row, int x_dt, int H, const uint8_t* w_ga
     return 0;
 }
 
+int orc_linear_q4_0(const void* x, int x_dt, int64_t T, int H, const uint8_t* w, int R, double* y) {
+    if (T < 0 || H <= 0 || H % 32 || R <= 0 || !x || !w || !y) return 1;
+    int nb = H / 32;
+    size_t row = (size_t)nb * 18, esz = (x_dt == ORC_F32) ? 4 : 2;
+    double* xv = (double*)malloc(sizeof(double) * (size_t)H);
+    if (!xv) return 2;
+    for (int64_t t = 0; t < T; ++t) {
+        const uint8_t* xr = (const uint8_t*)x + (size_t)t * (size_t)H * esz;
+        for (int j = 0; j < H; ++j) xv[j] = orc_load_act(xr, x_dt, j);
+        for (int r = 0; r < R; ++r) y[(size_t)t * R + r] = q4_0_row_dot(w + (size_t)r * row, nb, xv);
+    }
+    free(xv);
+    return 0;
+}
+
 int orc_expert_ffn(const void* x, int x_dt, int64_t T, int H, const uint8_t* w_gate_up,
                    const uint8_t* w_down, int I, int E, int K, const int32_t* offsets,
                    const int32_t* sorted_slots, const uint8_t* slot_mask, double* y_sorted) {

@@ -76,6 +76,12 @@ int orc_permute(const int32_t* ids, int64_t T, int K, int E, int32_t* offsets,
 int orc_expert_ffn_token(const void* x_row, int x_dt, int H, const uint8_t* w_gate_up,
                          const uint8_t* w_down, int I, int e, double* h_out, double* y_out);
 
+/* Q4_0 linear layer: y[t,r] = sum_j W[r,j] x[t,j] for r < R, W a matrix of R
+ * rows of H/32 Q4_0 blocks used in place (model card, table "What is inside":
+ * the Q, K and V rows of a block are one Q4_0 parent, like the experts'), fp64
+ * accumulation; y is [T, R]. */
+int orc_linear_q4_0(const void* x, int x_dt, int64_t T, int H, const uint8_t* w, int R, double* y);
+
 /* y_sorted[p,:] = expert output for slot sorted_slots[p] (expert owning position p).
  * slot_mask (nullable, indexed by slot) restricts the work to selected slots;
  * rows of unselected slots are left untouched. */

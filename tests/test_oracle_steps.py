@@ -142,6 +142,31 @@ def test_expert_ffn_token_equals_dense_f32():
             np.testing.assert_allclose(y, yr, rtol=1e-10, atol=1e-10)
 
 
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_linear_q4_0_equals_dense_matmul(act):
+    # the plain Q4_0 linear layer against whole-matrix decoding and a numpy fp64
+    # matmul; ragged row count, several tokens
+    L = tiny(T=3)
+    rng = np.random.default_rng(9)
+    w = L.w_down[1][:37]                         # 37 rows of 2 blocks (H = 64)
+    H = w.shape[1] * 32
+    x = rng.standard_normal((4, H)).astype(np.float32)
+    if act == "bf16":
+        x = synth.f32_to_bf16_bits(x)
+    y = oracle.linear_q4_0(x, w)
+    ref = act_to_f64(x) @ dequant_q4_0(w).T
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+    # a single non-zero weight block picks out d * (q - 8) . x of its 32 elements
+    w1 = np.zeros((2, H // 32, 18), np.uint8)
+    w1[1, 1, 0:2] = np.frombuffer(np.float16(0.5).tobytes(), np.uint8)
+    w1[1, 1, 2:] = 0x9A                           # low nibble 10, high nibble 9
+    y1 = oracle.linear_q4_0(x, w1)
+    xs = act_to_f64(x)[:, 32:64]
+    np.testing.assert_allclose(y1[:, 0], 0.0, atol=0)
+    np.testing.assert_allclose(y1[:, 1], 0.5 * (2 * xs[:, :16].sum(1) + 1 * xs[:, 16:].sum(1)),
+                               rtol=1e-12, atol=1e-12)
+
+
 def test_expert_ffn_token_bf16_hidden_rounding():
     L = tiny(T=2, act="bf16")
     x64 = act_to_f64(L.x)
