@@ -50,6 +50,7 @@ extern "C" {
 #define MOE_MAX_K 16
 #define MOE_MAX_H 4096
 #define MOE_MAX_I 4096
+#define MOE_MAX_LINEAR_ROWS 65536
 
 typedef enum {
     MOE_OK = 0,
@@ -159,6 +160,26 @@ moe_status moe_expert_ffn_q4_0(const void* x, int x_dt, int64_t T, int32_t H,
                                int32_t K, const int32_t* expert_offsets,
                                const int32_t* sorted_slots, float* y_sorted, void* ws,
                                size_t ws_bytes, void* stream);
+
+/*
+ * Plain Q4_0 linear layer (model card table "What is inside": the Q, K and V
+ * rows of a block form one Q4_0 parent, stored and multiplied like the
+ * experts' matrices).
+ *
+ *   x   [T, H] of type x_dt (fp32 or bf16), H % 32 == 0, H <= MOE_MAX_I
+ *   W   raw Q4_0 bytes [R rows][H/32 blocks][18], read in place;
+ *       1 <= R <= MOE_MAX_LINEAR_ROWS
+ *   y   [T, R] fp32 OUTPUT: y[t, r] = sum_j W[r, j] x[t, j]
+ *   ws  >= moe_linear_q4_0_workspace_bytes(T, H, R, x_dt) bytes, 16-byte
+ *       aligned; contents need no initialisation
+ * The same kernels as the experts' down product (one expert holding every
+ * token): Q4_0 GEMV with exact integer block products for few tokens, exact
+ * bf16 MFMA products for bf16 activations from 64 tokens (H % 64 == 0 and
+ * R % 16 == 0); fp32 accumulation, weights never rounded.
+ */
+size_t moe_linear_q4_0_workspace_bytes(int64_t T, int32_t H, int32_t R, int x_dt);
+moe_status moe_linear_q4_0(const void* x, int x_dt, int64_t T, int32_t H, const void* W,
+                           int32_t R, float* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Weighted combine (model card table "What is inside": FP32 expert scales).

@@ -40,6 +40,8 @@ SIGNATURES = {
     "moe_combine": ([_P, _P, _P, _P, _P, _I64, _I32, _I32, _P, C.c_int, _P, _P, C.c_int, _P],
                     C.c_int),
     "moe_rmsnorm": ([_P, C.c_int, _P, _F32, _I64, _I32, _P, C.c_int, _P], C.c_int),
+    "moe_linear_q4_0_workspace_bytes": ([_I64, _I32, _I32, C.c_int], _SZ),
+    "moe_linear_q4_0": ([_P, C.c_int, _I64, _I32, _P, _I32, _P, _P, _SZ, _P], C.c_int),
 }
 
 
@@ -193,6 +195,29 @@ def moe_expert_ffn_q4_0(x: torch.Tensor, w_gate_up: torch.Tensor, w_down: torch.
                                    K, _ptr(expert_offsets), _ptr(sorted_slots), _ptr(y_sorted),
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "moe_expert_ffn_q4_0")
+
+
+def moe_linear_q4_0(x: torch.Tensor, w: torch.Tensor, y: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Plain Q4_0 linear layer y [T, R] (fp32) = x [T, H] W^T; w is uint8 [R, H/32, 18]
+    (raw Q4_0 bytes, e.g. a block's Q, K and V rows as one parent)."""
+    T, H = x.shape
+    _dev(x, "x")
+    _dev(w, "w", torch.uint8)
+    R = w.shape[0]
+    if w.numel() != R * (H // 32) * 18:
+        raise ValueError("Q4_0 weight size disagrees with [R][H/32][18]")
+    if y is None:
+        y = torch.empty((T, R), dtype=torch.float32, device=x.device)
+    _dev(y, "y", torch.float32)
+    if tuple(y.shape) != (T, R):
+        raise ValueError("y must be [T, R]")
+    if ws is None:
+        nb = max(16, lib.moe_linear_q4_0_workspace_bytes(T, H, R, act_dtype(x)))
+        ws = torch.empty((nb,), dtype=torch.uint8, device=x.device)
+    _check(lib.moe_linear_q4_0(_ptr(x), act_dtype(x), T, H, _ptr(w), R, _ptr(y), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(stream)), "moe_linear_q4_0")
+    return y
 
 
 _DENSE_INDEX = {}

@@ -172,6 +172,41 @@ moe_status moe_expert_ffn_q4_0(const void* x, int x_dt, int64_t T, int32_t H,
                                            (hipStream_t)stream));
 }
 
+size_t moe_linear_q4_0_workspace_bytes(int64_t T, int32_t H, int32_t R, int x_dt) {
+    if (T < 0 || T > (int64_t)0x7FFFFFFF || check_dim(H, MOE_MAX_I) != MOE_OK || R < 1 ||
+        R > MOE_MAX_LINEAR_ROWS || !dtype_ok(x_dt))
+        return 0;
+    // [0, 256): offsets {0, T}; then the slot list 0..T-1; then, on the MFMA
+    // path, the activations in MFMA block order with their block sums
+    size_t b = 256 + round_up((size_t)T * 4, 256);
+    if (moe::linear_use_mfma(x_dt, T, H, R)) b += moe::linear_mfma_ws_bytes(T, H);
+    return b;
+}
+
+moe_status moe_linear_q4_0(const void* x, int x_dt, int64_t T, int32_t H, const void* W,
+                           int32_t R, float* y, void* ws, size_t ws_bytes, void* stream) {
+    if (T < 0 || T > (int64_t)0x7FFFFFFF || R < 1 || R > MOE_MAX_LINEAR_ROWS) return MOE_ERR_SHAPE;
+    moe_status s = check_dim(H, MOE_MAX_I);
+    if (s != MOE_OK) return s;
+    if (!dtype_ok(x_dt)) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!x || !W || !y) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(W) || !aligned16(y)) return MOE_ERR_ALIGN;
+    const size_t need = moe_linear_q4_0_workspace_bytes(T, H, R, x_dt);
+    if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    int32_t* offsets = (int32_t*)ws;
+    int32_t* slots = (int32_t*)((uint8_t*)ws + 256);
+    if ((s = hip_status(moe::launch_dense_index(T, offsets, slots, st))) != MOE_OK) return s;
+    if (moe::linear_use_mfma(x_dt, T, H, R))
+        return hip_status(moe::launch_linear_mfma(x, T, H, (const uint8_t*)W, R, offsets, slots,
+                                                  (uint8_t*)ws + 256 + round_up((size_t)T * 4, 256),
+                                                  y, st));
+    return hip_status(moe::launch_linear_gemv(x, x_dt, T, H, (const uint8_t*)W, R, offsets, slots,
+                                              y, st));
+}
+
 moe_status moe_combine(const float* y_sorted, const int32_t* slot_pos, const int32_t* topk_ids,
                        const float* topk_w, const float* expert_scale, int64_t T, int32_t K,
                        int32_t H, const void* residual, int residual_dt, float* out_f32,

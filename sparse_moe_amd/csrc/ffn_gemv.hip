@@ -528,4 +528,40 @@ hipError_t launch_ffn_gemv(const void* x, int x_dt, int64_t T, int H, const uint
     return hipGetLastError();
 }
 
+// ---- plain Q4_0 linear layer: y [T, R] = x [T, H] W^T --------------------------
+// The down-product kernels with one expert holding every token in order
+// (offsets {0, T}, slots 0..T-1, written by dense_index).
+__global__ void dense_index(int64_t T, int32_t* __restrict__ offsets, int32_t* __restrict__ slots) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < T) slots[i] = (int32_t)i;
+    if (i == 0) {
+        offsets[0] = 0;
+        offsets[1] = (int32_t)T;
+    }
+}
+
+hipError_t launch_dense_index(int64_t T, int32_t* offsets, int32_t* slots, hipStream_t st) {
+    dense_index<<<(unsigned)((T + 255) / 256), 256, 0, st>>>(T, offsets, slots);
+    return hipGetLastError();
+}
+
+hipError_t launch_linear_gemv(const void* x, int x_dt, int64_t T, int H, const uint8_t* W, int R,
+                              const int32_t* offsets, const int32_t* slots, float* y,
+                              hipStream_t st) {
+    auto go = [&](auto adt, auto tc, auto direct) {
+        launch_lpr<1, decltype(adt)::value, decltype(tc)::value, decltype(direct)::value, false>(
+            W, H / 32, H, R, x, offsets, slots, 1, 1, 1, y, st);
+    };
+    using F32 = std::integral_constant<int, MOE_F32>;
+    using BF16 = std::integral_constant<int, MOE_BF16>;
+    using One = std::integral_constant<int, 1>;
+    using Two = std::integral_constant<int, 2>;
+    const bool f32 = x_dt == MOE_F32;
+    if (T == 1)
+        f32 ? go(F32{}, One{}, std::false_type{}) : go(BF16{}, One{}, std::false_type{});
+    else
+        f32 ? go(F32{}, Two{}, std::true_type{}) : go(BF16{}, Two{}, std::true_type{});
+    return hipGetLastError();
+}
+
 }  // namespace moe

@@ -450,4 +450,23 @@ hipError_t launch_ffn_mfma(const void* x, int64_t T, int H, const uint8_t* w_gat
     return hipGetLastError();
 }
 
+size_t linear_mfma_ws_bytes(int64_t T, int H) {
+    return align256((size_t)T * H * 2) + align256((size_t)T * (H / 32) * 4);
+}
+
+hipError_t launch_linear_mfma(const void* x, int64_t T, int H, const uint8_t* W, int R,
+                              const int32_t* offsets, const int32_t* slots, void* ws, float* y,
+                              hipStream_t st) {
+    uint16_t* xp = (uint16_t*)ws;
+    float* xs = (float*)((uint8_t*)ws + align256((size_t)T * H * 2));
+    const int64_t nblk = T * (H / 32);
+    ffn_mfma_prep<<<(unsigned)((nblk + 255) / 256), 256, 0, st>>>((const uint16_t*)x, nblk, xp, xs);
+    const int N = (int)T, mtiles = N / MT + 1;
+    const int n_tiles = (R + NT - 1) / NT;
+    const int total = (mtiles * n_tiles + 7) / 8 * 8;
+    ffn_mfma<1><<<total, 256, LDS_BYTES, st>>>(xp, xs, W, H / 32, R, R, n_tiles, offsets, slots, 1,
+                                               1, nullptr, nullptr, y);
+    return hipGetLastError();
+}
+
 }  // namespace moe

@@ -41,6 +41,19 @@ hipError_t launch_ffn_mfma(const void* x, int64_t T, int H, const uint8_t* w_gat
                            const int32_t* offsets, const int32_t* sorted_slots, void* ws,
                            float* y_sorted, hipStream_t st);
 
+// plain Q4_0 linear layer y [T, R] = x [T, H] W^T on the down-product kernels
+inline bool linear_use_mfma(int x_dt, int64_t T, int H, int R) {
+    return x_dt == MOE_BF16 && T >= FFN_MFMA_MIN_T && H % 64 == 0 && R % 16 == 0;
+}
+hipError_t launch_dense_index(int64_t T, int32_t* offsets, int32_t* slots, hipStream_t st);
+hipError_t launch_linear_gemv(const void* x, int x_dt, int64_t T, int H, const uint8_t* W, int R,
+                              const int32_t* offsets, const int32_t* slots, float* y,
+                              hipStream_t st);
+size_t linear_mfma_ws_bytes(int64_t T, int H);
+hipError_t launch_linear_mfma(const void* x, int64_t T, int H, const uint8_t* W, int R,
+                              const int32_t* offsets, const int32_t* slots, void* ws, float* y,
+                              hipStream_t st);
+
 hipError_t launch_combine(const float* y, const int32_t* slot_pos, const int32_t* ids,
                           const float* w, const float* scale, int64_t T, int K, int H,
                           const void* residual, int rdt, float* out_f32, void* out_act, int odt,

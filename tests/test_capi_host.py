@@ -120,3 +120,23 @@ def test_combine_and_rmsnorm_validation():
     assert g(A, 1, A, C.c_float(-1.0), 4, 256, A, 1, None) == SHAPE
     assert g(A, 1, A, C.c_float(1e-6), 4, 256, MIS, 1, None) == ALIGN
     assert g(None, 1, None, C.c_float(1e-6), 0, 256, None, 1, None) == OK
+
+
+def test_linear_validation_and_workspace():
+    f = lib.moe_linear_q4_0
+    small = lib.moe_linear_q4_0_workspace_bytes(4, 2816, 4224, 0)
+    assert small == 256 + 256                      # offsets, slot list (GEMV path)
+    big = lib.moe_linear_q4_0_workspace_bytes(4096, 2816, 4224, 1)
+    assert big >= 256 + 4096 * 4 + 4096 * 2816 * 2 + 4096 * 88 * 4   # + MFMA staging
+    assert lib.moe_linear_q4_0_workspace_bytes(4, 250, 16, 0) == 0    # H % 32
+    assert lib.moe_linear_q4_0_workspace_bytes(4, 2816, 0, 0) == 0    # no rows
+    # (x, x_dt, T, H, W, R, y, ws, ws_bytes, stream)
+    assert f(A, 0, 4, 2816, A, 4224, A, A, 16, None) == WS
+    assert f(A, 0, 4, 2816, A, 4224, A, None, small, None) == WS
+    assert f(A, 0, 4, 2800, A, 4224, A, A, small, None) == SHAPE
+    assert f(A, 0, 4, 8192, A, 4224, A, A, small, None) == SHAPE      # H > max
+    assert f(A, 0, 4, 2816, A, 70000, A, A, small, None) == SHAPE     # R > max
+    assert f(A, 0, 4, 2816, None, 4224, A, A, small, None) == NULL
+    assert f(A, 0, 4, 2816, A, 4224, MIS, A, small, None) == ALIGN
+    assert f(A, 7, 4, 2816, A, 4224, A, A, small, None) == UNSUP
+    assert f(None, 0, 0, 2816, None, 4224, None, None, 0, None) == OK
