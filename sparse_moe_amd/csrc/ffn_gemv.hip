@@ -172,9 +172,13 @@ MOE_DEV void store_span(uint8_t* lds_wave, int lane, const u32x4a4 (&v)[NCH]) {
 }
 
 // steps per wave: gate/up waves cover 2 output rows (row pairs), down waves 8
-template <int MODE, int LPR>
+constexpr int DIRECT_ROW_MULT = 2;
+// (twice that with direct register windows: no LDS span to size, and the
+// longer stream per workgroup pays for its fixed latency)
+template <int MODE, int LPR, bool DIRECT>
 constexpr int steps_per_wave() {
-    return (MODE == 0) ? ((64 / LPR) >= 2 ? 1 : 2 / (64 / LPR)) : ((64 / LPR) >= 8 ? 1 : 8 / (64 / LPR));
+    constexpr int rows = ((MODE == 0) ? 2 : 8) * (DIRECT ? DIRECT_ROW_MULT : 1);
+    return (64 / LPR) >= rows ? 1 : rows / (64 / LPR);
 }
 
 // ---- kernel --------------------------------------------------------------------
@@ -451,7 +455,7 @@ static void launch_mode(const uint8_t* W, int nb, int I, int H, const void* act,
                         const int32_t* offsets, const int32_t* sorted_slots, int K, int E,
                         int n_active, void* out, hipStream_t st) {
     constexpr int RPS = 64 / LPR;
-    constexpr int UPW = steps_per_wave<MODE, LPR>();
+    constexpr int UPW = steps_per_wave<MODE, LPR, DIRECT>();
     constexpr int RPW = RPS * UPW;
     constexpr int NR = (MODE == 0) ? 2 : 1;
     const int rows_out = (MODE == 0) ? I : H;
