@@ -79,25 +79,75 @@ hipError_t launch_combine(const float* y, const int32_t* slot_pos, const int32_t
 }
 
 // out[t,:] = x[t,:] * (mean x^2 + eps)^-1/2 * w, fp32, rounded to out dtype.
+// One workgroup per token; a thread holds chunks c and c + 256 of 8 consecutive
+// elements (H <= 4096) in registers, so the row is read once, with 16-byte
+// loads, and written with 16-byte stores.
+template <int XDT>
+MOE_DEV void load8(const void* x, int64_t e0, float v[8]) {
+    if (XDT == MOE_F32) {
+        const float4 a = *reinterpret_cast<const float4*>((const float*)x + e0);
+        const float4 b = *reinterpret_cast<const float4*>((const float*)x + e0 + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+        const uint4 u = *reinterpret_cast<const uint4*>((const uint16_t*)x + e0);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    }
+}
+
+template <int ODT>
+MOE_DEV void store8(void* out, int64_t e0, const float v[8]) {
+    if (ODT == MOE_F32) {
+        *reinterpret_cast<float4*>((float*)out + e0) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>((float*)out + e0 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+        *reinterpret_cast<uint4*>((uint16_t*)out + e0) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
 template <int XDT, int ODT>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ x,
                                                       const float* __restrict__ wt, float eps,
                                                       int H, void* __restrict__ out) {
     const int64_t t = blockIdx.x;
     __shared__ float part[4];
+    const int nch = H >> 3;
+    float v[2][8];
     float ss = 0.f;
-    for (int j = threadIdx.x; j < H; j += 256) {
-        const float v = load_act(x, XDT, t * H + j);
-        ss = fmaf(v, v, ss);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int c = threadIdx.x + 256 * r;
+        if (c < nch) {
+            load8<XDT>(x, t * H + 8 * c, v[r]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss = fmaf(v[r][i], v[r][i], ss);
+        }
     }
     ss = wave_sum(ss);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
     __syncthreads();
     const float tot = (part[0] + part[1]) + (part[2] + part[3]);
-    const float r = 1.0f / sqrtf(tot / (float)H + eps);
-    for (int j = threadIdx.x; j < H; j += 256) {
-        const float v = load_act(x, XDT, t * H + j);
-        store_act(out, ODT, t * H + j, (v * r) * wt[j]);
+    const float rs = 1.0f / sqrtf(tot / (float)H + eps);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int c = threadIdx.x + 256 * r;
+        if (c < nch) {
+            const float4 w0 = *reinterpret_cast<const float4*>(wt + 8 * c);
+            const float4 w1 = *reinterpret_cast<const float4*>(wt + 8 * c + 4);
+            const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+            float o[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = (v[r][i] * rs) * wv[i];
+            store8<ODT>(out, t * H + 8 * c, o);
+        }
     }
 }
 

@@ -322,19 +322,20 @@ MOE_DEV void split3(const float (&w)[8], ru32x4& hi, ru32x4& mid, ru32x4& lo) {
     }
 }
 
-__global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __restrict__ x, int T, int H,
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void router_logits_mfma(const uint16_t* __restrict__ x, int T, int H,
                                                           const float* __restrict__ W,
                                                           const float* __restrict__ rsc,
                                                           const float* __restrict__ bias, int E,
                                                           float* __restrict__ logits) {
-    __shared__ f32x4 part[3][4][64];
+    __shared__ f32x4 part[NW - 1][4][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l16 = lane & 15, g = lane >> 4;
     const int t0 = blockIdx.x * 32;
     const int e0 = blockIdx.y * 32;
-    // this wave's quarter of H (H is a multiple of 32)
+    // this wave's share of H (H is a multiple of 32)
     const int nsteps = H >> 5;
-    const int k_begin = (nsteps * wave / 4) * 32, k_end = (nsteps * (wave + 1) / 4) * 32;
+    const int k_begin = (nsteps * wave / NW) * 32, k_end = (nsteps * (wave + 1) / NW) * 32;
     // A operand: lane (token row l16, k group g); B operand: lane (expert column l16, k group g)
     const uint16_t* xa = x + (int64_t)min(t0 + l16, T - 1) * H + 8 * g;
     const uint16_t* xb = x + (int64_t)min(t0 + 16 + l16, T - 1) * H + 8 * g;
@@ -391,7 +392,7 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
         acc3 = rmfma(cur.b, lo1, acc3);
         cur = nxt;
     }
-    // partial sums of waves 1..3 to LDS; wave 0 adds them in order and stores
+    // partial sums of waves 1..NW-1 to LDS; wave 0 adds them in order and stores
     if (wave > 0) {
         part[wave - 1][0][lane] = acc0;
         part[wave - 1][1][lane] = acc1;
@@ -401,7 +402,7 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
     __syncthreads();
     if (wave > 0) return;
 #pragma unroll
-    for (int w = 0; w < 3; ++w) {
+    for (int w = 0; w < NW - 1; ++w) {
         acc0 += part[w][0][lane];
         acc1 += part[w][1][lane];
         acc2 += part[w][2][lane];
@@ -427,9 +428,16 @@ hipError_t launch_router_logits(const void* x, int x_dt, int64_t T, int H, const
                                 const float* rsc, const float* bias, int E, float* logits,
                                 hipStream_t st) {
     if (x_dt == MOE_BF16 && T >= ROUTER_MFMA_MIN_T && E % 32 == 0) {
+        // K split over the 4 waves of a workgroup, over 8 when the tiles are too
+        // few to fill the chip
         dim3 grid((unsigned)((T + 31) / 32), E / 32);
-        router_logits_mfma<<<grid, 256, 0, st>>>((const uint16_t*)x, (int)T, H, W, rsc, bias, E,
-                                                 logits);
+        const int64_t wgs = (int64_t)grid.x * grid.y;
+        if (wgs <= 128)
+            router_logits_mfma<8><<<grid, 512, 0, st>>>((const uint16_t*)x, (int)T, H, W, rsc, bias,
+                                                        E, logits);
+        else
+            router_logits_mfma<4><<<grid, 256, 0, st>>>((const uint16_t*)x, (int)T, H, W, rsc, bias,
+                                                        E, logits);
     } else if (T < ROUTER_MFMA_MIN_T) {
         dim3 grid(E, (unsigned)((T + ROUTER_GEMV_MAX_T - 1) / ROUTER_GEMV_MAX_T));
         router_variant(x_dt, (int)T, rsc != nullptr, [&](auto xdt, auto tt, auto r) {
