@@ -70,6 +70,22 @@ def test_shape_sweep(T, E, K):
     _run(L, token_sample=sample, fused_route=(T <= 8))
 
 
+@pytest.mark.parametrize("H,I,E,K,T,act", [
+    (4096, 4096, 16, 16, 3, "f32"),     # largest H, I and K (K = E): GEMV path
+    (4096, 4096, 16, 16, 64, "bf16"),   # the same on the bf16 MFMA path
+    (256, 128, 256, 16, 40, "bf16"),    # the most experts: GEMV path
+    (256, 128, 256, 16, 160, "bf16"),   # the most experts: MFMA path, one-slot tiles
+])
+def test_maximum_sizes(H, I, E, K, T, act):
+    # the library's limits (MOE_MAX_H, MOE_MAX_I, MOE_MAX_E, MOE_MAX_K), on
+    # sampled tokens where the oracle is slow
+    spec = synth.LayerSpec("max-H%d-I%d-E%d-K%d-T%d" % (H, I, E, K, T), H=H, E=E, K=K, I=I, T=T,
+                           act=act, router_std=1 / np.sqrt(H), seed=17)
+    L = synth.make_layer(spec)
+    sample = None if H < 1024 and T <= 40 else np.unique(np.r_[0, T // 2, T - 1])
+    _run(L, token_sample=sample, fused_route=(T * K <= 1024 and T <= 8))
+
+
 def test_fused_route_repeated_calls_reset_the_counter():
     # the fused routing kernel leaves its completion counter at zero: many calls in a
     # row on one workspace keep giving the oracle's routing
