@@ -115,59 +115,87 @@ MOE_DEV void topk_load(const float* l, int E, float (&v)[4]) {
     }
 }
 
-MOE_DEV void topk_select(const float (&lv)[4], int E, int K, int32_t* ids, float* w) {
+// NT tokens at once (one wave): the K rounds of the tokens are interleaved so
+// that their dependent DPP reductions overlap; each token's operations are
+// those of a single-token selection.
+template <int NT>
+MOE_DEV void topk_select_n(const float (&lv)[NT][4], int E, int K, int32_t* const (&ids)[NT],
+                           float* const (&w)[NT]) {
     const int lane = threadIdx.x & 63;
-    float v[4];
-    bool live[4];
+    float v[NT][4];
+    bool live[NT][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        live[i] = lane + 64 * i < E;
-        v[i] = live[i] ? lv[i] + 0.f : -INFINITY;  // + 0 turns -0 into +0
-    }
-    float selv[MOE_MAX_K];
-    int seli[MOE_MAX_K];
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            live[n][i] = lane + 64 * i < E;
+            v[n][i] = live[n][i] ? lv[n][i] + 0.f : -INFINITY;  // + 0 turns -0 into +0
+        }
+    float selv[NT][MOE_MAX_K];
+    int seli[NT][MOE_MAX_K];
 #pragma unroll
     for (int k = 0; k < MOE_MAX_K; ++k) {
-        selv[k] = 0.f;
-        seli[k] = 0;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            selv[n][k] = 0.f;
+            seli[n][k] = 0;
+        }
         if (k < K) {
-            float m = -INFINITY;
+            float m[NT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (live[i]) m = fmaxf(m, v[i]);
-            m = wave_max(m);
-            int idx = -1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint64_t bal = __ballot(live[i] && v[i] == m);
-                if (idx < 0 && bal) idx = 64 * i + (int)__builtin_ctzll(bal);
-            }
-            if (idx < 0) idx = 0;  // only when every remaining logit is NaN
-            selv[k] = m;
-            seli[k] = idx;
-            if ((idx & 63) == lane) {
+            for (int n = 0; n < NT; ++n) {
+                m[n] = -INFINITY;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (i == (idx >> 6)) live[i] = false;
+                    if (live[n][i]) m[n] = fmaxf(m[n], v[n][i]);
+            }
+#pragma unroll
+            for (int n = 0; n < NT; ++n) m[n] = wave_max(m[n]);
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                int idx = -1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint64_t bal = __ballot(live[n][i] && v[n][i] == m[n]);
+                    if (idx < 0 && bal) idx = 64 * i + (int)__builtin_ctzll(bal);
+                }
+                if (idx < 0) idx = 0;  // only when every remaining logit is NaN
+                selv[n][k] = m[n];
+                seli[n][k] = idx;
+                if ((idx & 63) == lane) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (i == (idx >> 6)) live[n][i] = false;
+                }
             }
         }
     }
-    float s = 0.f;
 #pragma unroll
-    for (int k = 0; k < MOE_MAX_K; ++k)
-        if (k < K) s += expf(selv[k] - selv[0]);
-    float myv = 0.f;
-    int myi = 0;
+    for (int n = 0; n < NT; ++n) {
+        float s = 0.f;
 #pragma unroll
-    for (int k = 0; k < MOE_MAX_K; ++k)
-        if (k == lane) {
-            myv = selv[k];
-            myi = seli[k];
+        for (int k = 0; k < MOE_MAX_K; ++k)
+            if (k < K) s += expf(selv[n][k] - selv[n][0]);
+        float myv = 0.f;
+        int myi = 0;
+#pragma unroll
+        for (int k = 0; k < MOE_MAX_K; ++k)
+            if (k == lane) {
+                myv = selv[n][k];
+                myi = seli[n][k];
+            }
+        if (lane < K) {
+            ids[n][lane] = myi;
+            w[n][lane] = expf(myv - selv[n][0]) / s;
         }
-    if (lane < K) {
-        ids[lane] = myi;
-        w[lane] = expf(myv - selv[0]) / s;
     }
+}
+
+MOE_DEV void topk_select(const float (&lv)[4], int E, int K, int32_t* ids, float* w) {
+    const float (&l1)[1][4] = *reinterpret_cast<const float (*)[1][4]>(&lv);
+    int32_t* const i1[1] = {ids};
+    float* const w1[1] = {w};
+    topk_select_n<1>(l1, E, K, i1, w1);
 }
 
 template <bool COH = false>

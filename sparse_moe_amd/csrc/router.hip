@@ -240,13 +240,20 @@ __global__ __launch_bounds__(256) void route_small(const void* __restrict__ x, i
     }
     __syncthreads();
     if (!s_last) return;
-    // wave w takes tokens w and w + 4: both tokens' logits are loaded first
-    float v0[4], v1[4];
+    // wave w takes tokens w and w + 4 (both selections interleaved)
     const int t0 = wave, t1 = wave + 4;
-    if (t0 < T) topk_load<true>(logits + (int64_t)t0 * E, E, v0);
-    if (t1 < T) topk_load<true>(logits + (int64_t)t1 * E, E, v1);
-    if (t0 < T) topk_select(v0, E, K, ids + t0 * K, w + t0 * K);
-    if (t1 < T) topk_select(v1, E, K, ids + t1 * K, w + t1 * K);
+    if (t1 < T) {
+        float v[2][4];
+        topk_load<true>(logits + (int64_t)t0 * E, E, v[0]);
+        topk_load<true>(logits + (int64_t)t1 * E, E, v[1]);
+        int32_t* const ip[2] = {ids + t0 * K, ids + t1 * K};
+        float* const wp[2] = {w + t0 * K, w + t1 * K};
+        topk_select_n<2>(v, E, K, ip, wp);
+    } else if (t0 < T) {
+        float v[4];
+        topk_load<true>(logits + (int64_t)t0 * E, E, v);
+        topk_select(v, E, K, ids + t0 * K, w + t0 * K);
+    }
     __syncthreads();  // ids of every token are written
     permute_block(ids, T * K, E, offsets, sorted_slots, slot_pos);
     if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
