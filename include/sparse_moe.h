@@ -16,7 +16,10 @@
  *   moe_permute          stable counting sort of the T*K (token, k) slots by expert
  *   moe_expert_ffn_q4_0  per slot: h = GELU_tanh(x Wg^T) * (x Wu^T), y = h Wd^T
  *   moe_combine          out[t] = sum_k w[t,k] * scale[e] * y[slot]
- * plus moe_rmsnorm, the pre-norm of a stack of such layers.
+ * moe_route does the first two in one call (one kernel for up to 8 tokens).
+ * Also: moe_rmsnorm, the pre-norm of a stack of such layers, and
+ * moe_linear_q4_0, a plain Q4_0 linear layer on the same kernels (a block's
+ * Q, K, V parent).
  *
  * Conventions shared by every call:
  *  - Pointers are DEVICE pointers owned by the caller (unless a parameter says
@@ -34,6 +37,10 @@
  *  - Calls are thread-safe; calls that share a workspace must be ordered on
  *    one stream.
  *  - Results are deterministic: the same inputs give bitwise the same outputs.
+ *  - Below 64 tokens a token's logits, top-K and outputs do not depend on the
+ *    other tokens of the batch (bitwise), so a verification batch reproduces
+ *    the single-token decode (model card, sections "Speculative decoding" and
+ *    "Quality").
  */
 #ifndef SPARSE_MOE_H
 #define SPARSE_MOE_H

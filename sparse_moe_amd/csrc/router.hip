@@ -15,13 +15,6 @@ namespace moe {
 // all issued at once) and dots it with up to ROUTER_GEMV_MAX_T tokens.
 constexpr int ROUTER_MAX_CHUNKS = MOE_MAX_H / 256;  // float4 chunks of 64 lanes per row
 
-MOE_DEV float4 load_x4(const void* x, int xdt, int64_t i4) {
-    if (xdt == MOE_F32) return reinterpret_cast<const float4*>(x)[i4];
-    const uint2 b = reinterpret_cast<const uint2*>(x)[i4];
-    return make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
-                       __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
-}
-
 // One expert per workgroup: wave w takes a quarter of the float4 chunks of the
 // expert's W_r row, dots them with every token and leaves its per-token partial
 // sums in part[w][t].  Every load (W_r, router scale, the TT token rows) is
@@ -204,7 +197,7 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ lo
 
 
 // Few tokens, routing fused into one kernel: the router GEMV by every
-// workgroup (one wave per expert, logits written with coherent stores), then
+// workgroup (one expert each, logits written with coherent stores), then
 // the last workgroup to finish (counted with an agent-scope atomic in the
 // workspace) runs top-K for every token on coherently loaded logits and the
 // permutation of the T*K slots, and resets the counter to zero.
