@@ -19,6 +19,93 @@ __global__ __launch_bounds__(256) void permute_single(const int32_t* __restrict_
     permute_block(ids, N, E, offsets, sorted_slots, slot_pos);
 }
 
+// Up to PERM_WIDE slots in one launch: one workgroup of 16 waves, 1024 slots
+// per round.  Each (round, wave) pair counts its slots per expert (wave match)
+// into its own row of a count table, so the rounds need no barriers between
+// them; an exclusive prefix down each expert's column (rows in slot order)
+// then gives every slot its stable rank, a scan over the experts the offsets.
+constexpr int PERM_WIDE = 4096;
+
+__global__ __launch_bounds__(1024) void permute_wide(const int32_t* __restrict__ ids, int N, int E,
+                                                     int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ sorted_slots,
+                                                     int32_t* __restrict__ slot_pos) {
+    constexpr int RMAX = PERM_WIDE / 1024;
+    __shared__ __align__(16) uint16_t cnt[RMAX * 16][MOE_MAX_E];
+    __shared__ int seg[4][MOE_MAX_E];
+    __shared__ int wsum[4];
+    __shared__ int off[MOE_MAX_E];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int rounds = (N + 1023) >> 10;
+    const int R16 = rounds * 16;
+    int ex[RMAX];
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+        const int s = r * 1024 + tid;
+        const int v = ids[min(s, N - 1)];
+        ex[r] = s < N ? v : -1;
+    }
+    uint4* z = reinterpret_cast<uint4*>(&cnt[0][0]);
+    for (int i = tid; i < R16 * MOE_MAX_E / 8; i += 1024) z[i] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    int rw[RMAX];
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+        rw[r] = 0;
+        if (r < rounds) {
+            const uint32_t key = ex[r] >= 0 ? (uint32_t)ex[r] : 256u;
+            const uint64_t m = match_key9(key);
+            rw[r] = __popcll(m & lanemask_lt());
+            if (ex[r] >= 0 && rw[r] == 0) cnt[r * 16 + wave][ex[r]] = (uint16_t)__popcll(m);
+        }
+    }
+    __syncthreads();
+    // column prefix: four threads per expert, each over a quarter of the rows
+    const int col = tid & (MOE_MAX_E - 1), sg = tid >> 8, per = R16 >> 2;
+    int sum = 0;
+    for (int i = 0; i < per; ++i) sum += cnt[sg * per + i][col];
+    seg[sg][col] = sum;
+    __syncthreads();
+    int base = 0;
+    for (int q = 0; q < sg; ++q) base += seg[q][col];
+    for (int i = 0; i < per; ++i) {
+        const int c = cnt[sg * per + i][col];
+        cnt[sg * per + i][col] = (uint16_t)base;
+        base += c;
+    }
+    // exclusive scan of the expert totals by the first four waves
+    int incl = 0, tot = 0;
+    if (tid < MOE_MAX_E) {
+        tot = col < E ? seg[0][col] + seg[1][col] + seg[2][col] + seg[3][col] : 0;
+        incl = tot;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(incl, d);
+            if (lane >= d) incl += y;
+        }
+        if (lane == 63) wsum[wave] = incl;
+    }
+    __syncthreads();
+    if (tid < MOE_MAX_E) {
+        for (int q = 0; q < wave; ++q) incl += wsum[q];
+        if (col < E) {
+            off[col] = incl - tot;
+            offsets[col] = incl - tot;
+        }
+        if (col == E - 1) offsets[E] = incl;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+        const int s = r * 1024 + tid;
+        if (ex[r] >= 0) {
+            const int pos = off[ex[r]] + cnt[r * 16 + wave][ex[r]] + rw[r];
+            sorted_slots[pos] = s;
+            slot_pos[s] = pos;
+        }
+    }
+}
+
 // Several tiles: per-tile stable ranks and per-expert tile counts.
 __global__ __launch_bounds__(256) void permute_tiles(const int32_t* __restrict__ ids, int N, int E,
                                                      int32_t* __restrict__ tile_counts,
@@ -105,7 +192,7 @@ __global__ __launch_bounds__(256) void permute_scatter(const int32_t* __restrict
 }
 
 size_t permute_ws_bytes(int64_t N, int E) {
-    if (N <= PERM_TILE) return 0;
+    if (N <= PERM_WIDE) return 0;
     const int64_t ntiles = (N + PERM_TILE - 1) / PERM_TILE;
     return (size_t)(2 * ntiles * E + N) * sizeof(int32_t);
 }
@@ -114,6 +201,10 @@ hipError_t launch_permute(const int32_t* ids, int N, int E, int32_t* offsets, in
                           int32_t* slot_pos, void* ws, hipStream_t st) {
     if (N <= PERM_TILE) {
         permute_single<<<1, 256, 0, st>>>(ids, N, E, offsets, sorted_slots, slot_pos);
+        return hipGetLastError();
+    }
+    if (N <= PERM_WIDE) {
+        permute_wide<<<1, 1024, 0, st>>>(ids, N, E, offsets, sorted_slots, slot_pos);
         return hipGetLastError();
     }
     const int ntiles = (N + PERM_TILE - 1) / PERM_TILE;
