@@ -43,6 +43,7 @@ constexpr int ROWB = 80;       // LDS bytes per (row, block): 64 data + 16 pad (
 // one LDS slot (a pair of blocks): activations [2][MT rows][80 B], sums [2][MT]
 constexpr int SLOT_BYTES = 2 * MT * ROWB + 2 * MT * 4;
 constexpr int LDS_BYTES = 2 * SLOT_BYTES;
+constexpr int LIGHT_DEPTH = 4;  // block pairs in flight in tiles of at most 64 slots
 
 // Position, inside a 32-element block as the MFMA reads it, of element j.
 // Lane group g holds k slots 8g..8g+7 = elements 4g, 4g+2, 4g+16, 4g+18,
@@ -226,11 +227,14 @@ __global__ __launch_bounds__(256) void ffn_mfma(
     };
 
     // The main loop and epilogue for MF slot fragments (16 slots each).  A tile
-    // of at most 32 slots (an expert's last, partial tile, or a small expert)
-    // runs with MF = 2: a quarter of the activation staging, MFMAs and scale
-    // FMAs of a full tile.
-    auto run = [&](auto mf_const) {
+    // of at most 32 (64) slots (an expert's last, partial tile, or a small
+    // expert) runs with MF = 2 (4): a quarter (half) of the activation staging,
+    // MFMAs and scale FMAs of a full tile.  Such a tile has too little work per
+    // block pair to hide a memory latency behind it, so it keeps P pairs of
+    // loads in flight (register rings of P stages) instead of one.
+    auto run = [&](auto mf_const, auto p_const) {
         constexpr int MF = decltype(mf_const)::value;
+        constexpr int P = decltype(p_const)::value;
         constexpr int NA = MF / 2;  // activation chunks per thread per pair (32 rows each)
         f32x4 acc[MF][4];
 #pragma unroll
@@ -300,19 +304,45 @@ __global__ __launch_bounds__(256) void ffn_mfma(
             }
         };
 
-        AStage RA;
-        BStage RB;
-        load_a(RA, 0);
-        load_b(RB, 0);
-        store_a(RA, 0);
-        load_a(RA, min(1, npairs - 1));
-        lds_barrier();
-        for (int j = 0; j < npairs; ++j) {
-            store_a(RA, (j + 1) & 1);
-            load_a(RA, min(j + 2, npairs - 1));
-            if (active) compute(j & 1, RB);
-            load_b(RB, min(j + 1, npairs - 1));
+        if constexpr (P == 1) {
+            AStage RA;
+            BStage RB;
+            load_a(RA, 0);
+            load_b(RB, 0);
+            store_a(RA, 0);
+            load_a(RA, min(1, npairs - 1));
             lds_barrier();
+            for (int j = 0; j < npairs; ++j) {
+                store_a(RA, (j + 1) & 1);
+                load_a(RA, min(j + 2, npairs - 1));
+                if (active) compute(j & 1, RB);
+                load_b(RB, min(j + 1, npairs - 1));
+                lds_barrier();
+            }
+        } else {
+            // at the start of pair j: LDS slot j & 1 holds pair j, RA[(j + 1) % P]
+            // pair j + 1, RB[j % P] pair j.  The pairs are run in groups of P (the
+            // ring index a constant); the ones past the end only load and store.
+            AStage RA[P];
+            BStage RB[P];
+            load_a(RA[0], 0);
+            store_a(RA[0], 0);
+#pragma unroll
+            for (int q = 1; q <= P; ++q) load_a(RA[q % P], min(q, npairs - 1));
+#pragma unroll
+            for (int q = 0; q < P; ++q) load_b(RB[q], min(q, npairs - 1));
+            lds_barrier();
+            for (int j0 = 0; j0 < npairs; j0 += P) {
+#pragma unroll
+                for (int u = 0; u < P; ++u) {
+                    const int j = j0 + u;
+                    store_a(RA[(u + 1) % P], (j + 1) & 1);
+                    load_a(RA[(u + 1) % P], min(j + 1 + P, npairs - 1));
+                    if (active && j < npairs) compute(j & 1, RB[u]);
+                    load_b(RB[u], min(j + P, npairs - 1));
+                    lds_barrier();
+                }
+            }
         }
 
         if (!active) return;
@@ -366,9 +396,11 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         }
     };
     if (cnt <= 32)
-        run(std::integral_constant<int, 2>{});
+        run(std::integral_constant<int, 2>{}, std::integral_constant<int, LIGHT_DEPTH>{});
+    else if (cnt <= 64)
+        run(std::integral_constant<int, 4>{}, std::integral_constant<int, LIGHT_DEPTH>{});
     else
-        run(std::integral_constant<int, 8>{});
+        run(std::integral_constant<int, 8>{}, std::integral_constant<int, 1>{});
 }
 
 // Activations -> MFMA block order, plus -1.5 * block sums.  One thread per

@@ -169,6 +169,7 @@ def test_deterministic_and_fully_written():
     (288, 96, 8, 2, 70, None),       # odd block counts per row (9 and 3): served by the GEMV path
     (256, 64, 8, 2, 600, None),      # ~150 slots per expert: two slot tiles per expert
     (256, 192, 4, 1, 300, None),     # K = 1, a partial second column tile of the gate/up product
+    (256, 128, 8, 2, 200, None),     # ~50 slots per expert: tiles of 33-64 slots
     (2816, 704, 128, 8, 64, None),   # Gemma shape at the smallest token count of the MFMA path
     # Zipf-skewed routing: experts of a few slots (one mostly empty tile) next
     # to experts of several tiles, as in the layer stack
