@@ -35,15 +35,30 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2a4 __attribute__((ext_vector_type(2), aligned(4)));
 
 constexpr int MT = 128;        // slots per tile
 constexpr int NT = 256;        // weight rows per tile (64 per wave)
-constexpr int ROWB = 80;       // LDS bytes per (row, block): 64 data + 16 pad (no bank conflicts)
-// one LDS slot (a pair of blocks): activations [2][MT rows][80 B], sums [2][MT]
-constexpr int SLOT_BYTES = 2 * MT * ROWB + 2 * MT * 4;
-constexpr int LDS_BYTES = 2 * SLOT_BYTES;
-constexpr int LIGHT_DEPTH = 4;  // block pairs in flight in tiles of at most 64 slots
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// s_waitcnt for vector memory only: vmcnt <= n (expcnt and lgkmcnt left alone)
+template <int N>
+MOE_DEV void wait_vmcnt() {
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier for the direct-load pipeline: waits for this wave's LDS
+// reads and writes (lgkmcnt) but not for its direct loads in flight, which a
+// memory-model fence would drain; the empty asm statements keep the compiler
+// from moving LDS accesses across it.  Completion of the direct loads a stage
+// needs is waited for explicitly (wait_vmcnt) before the barrier.
+MOE_DEV void stage_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt(63) and expcnt(7): no wait
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // Position, inside a 32-element block as the MFMA reads it, of element j.
 // Lane group g holds k slots 8g..8g+7 = elements 4g, 4g+2, 4g+16, 4g+18,
@@ -136,25 +151,42 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
 //
 // Tile: MT slots x NT weight rows; wave w owns weight rows 64w..64w+63 of the
 // tile (4 MFMA row fragments) against all MT slots (8 fragments), 128 fp32
-// accumulators per lane.  Each wave loads and unpacks its own weights straight
-// into registers (no LDS): per block pair and row fragment a lane reads 8 + 4
-// bytes of its row's 36-byte window; the two fp16 scales reach the lanes that
-// need them through ds_bpermute.  Only the activations and their block sums go
-// through LDS, shared by the four waves.
+// accumulators per lane.
 //
-// Pipeline over block pairs j: iteration j stores the activations of pair j+1
-// (loaded one iteration earlier) into LDS slot (j+1)&1, issues the loads of
-// the activations of pair j+2, runs the MFMAs of pair j, then loads the weights
-// of pair j+1 (one register set: a second set does not fit two waves per SIMD
-// and measured no faster), and ends on an LDS-only barrier.  Loads are unconditional
-// (clamped past the end) so the compiler's wait counts stay exact.
+// Every operand goes through LDS by direct loads (global_load_lds), two stages
+// in turn: iteration j issues the loads of pair j+1 into the stage pair j-1
+// used, runs the MFMAs of pair j, waits for its own loads and ends on a
+// barrier, so no register holds staged data.  A stage is the activations
+// [2 blocks][MT rows][64 B] (the 16-byte chunks of a row rotated by
+// (row >> 2) & 3, so the fragment reads are conflict-free), their block sums
+// [2][MT] and the tile's weight rows [NT][48 B] (a row's 36 bytes of the pair
+// as its bytes 0-15, 16-31 and 20-35: direct loads of 12 bytes would land 16
+// bytes apart, so three 16-byte loads that never cross the pair).  Each part
+// of each stage is its own LDS array and the loop runs two iterations per trip
+// with constant stage indices, so the compiler sees that the loads in flight
+// do not touch what is being read (with one array for both stages it waited
+// for every load before the reads).  The barrier is a bare s_barrier after an
+// LDS-only wait: a memory-model fence would also drain the direct loads.
+// Per wave and pair: MF/2 16-byte loads of activations (16 rows of one block
+// each), one 4-byte load of block sums (64 rows of one block) and three
+// 16-byte loads of weights (21 rows per instruction), in place of eight
+// per-lane weight loads that each touched 16 rows.  A third weight stage (two
+// pairs in flight) measured no faster.
 template <int MODE>
 __global__ __launch_bounds__(256) void ffn_mfma(
     const uint16_t* __restrict__ act, const float* __restrict__ csum, const uint8_t* __restrict__ W,
     int nb, int rows_e, int ncols, int n_tiles, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_slots, int K, int E, uint16_t* __restrict__ h_out,
     float* __restrict__ hsum_out, float* __restrict__ y_out) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ __attribute__((aligned(16))) uint8_t a0[2 * MT * 64], a1[2 * MT * 64];
+    __shared__ __attribute__((aligned(16))) float cc0[2 * MT], cc1[2 * MT];
+    __shared__ __attribute__((aligned(16))) uint8_t w0[NT * 48], w1[NT * 48];
+    struct StageRef {
+        uint8_t* a;
+        float* c;
+        uint8_t* w;
+    };
+    StageRef st0{a0, cc0, w0}, st1{a1, cc1, w1};
     __shared__ int s_res[4];
 
     int e, base, cnt, ntile;
@@ -180,105 +212,98 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         nfa = c0 < ncols ? 4 : 0;
     else
         nfa = max(0, min(4, (ncols - c0) >> 4));
-    uint32_t woff[4];  // byte offset (in the expert) of this lane's row, plus its qs group
+    // weight pieces: a row's 36 bytes of a pair as three 16-byte loads of its
+    // bytes 0-15, 16-31 and 20-35 (never past the pair), 48 bytes per row in
+    // LDS; lane piece i of a pair is q = 64 i + lane of the wave's 192 pieces,
+    // row 16 nf + l16 = q / 3 of the wave, piece q % 3
+    uint32_t woff[3];
 #pragma unroll
-    for (int nf = 0; nf < 4; ++nf) {
+    for (int i = 0; i < 3; ++i) {
+        const int q = 64 * i + lane, r = q / 3;
+        const int nf = r >> 4, rl = r & 15;
         int row;
         if (MODE == 0)
-            row = min(c0 + (nf & 1) * 16 + l16, ncols - 1) + (nf >> 1) * ncols;
+            row = min(c0 + (nf & 1) * 16 + rl, ncols - 1) + (nf >> 1) * ncols;
         else
-            row = min(c0 + nf * 16 + l16, rows_e - 1);
-        woff[nf] = (uint32_t)row * rowbytes + 4u * (uint32_t)g;
+            row = min(c0 + nf * 16 + rl, rows_e - 1);
+        const int pc = q % 3;
+        woff[i] = (uint32_t)row * rowbytes + (pc == 0 ? 0u : pc == 1 ? 16u : 20u);
     }
-
-    // ---- activation staging roles: 16-byte chunk ch of tile rows (tid>>3) + 32i ----
-    const int ch = tid & 7, srow = tid >> 3;
-    uint32_t aoff[4];  // element offset of (row, pair 0, chunk) in act
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = srow + 32 * i;
-        const int p = base + min(r, cnt - 1);
-        const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
-        aoff[i] = (uint32_t)(arow * nb * 32) + 8u * (uint32_t)ch;
-    }
-    uint32_t coff;  // block-sum offset of (tile row tid & 127, block tid >> 7 of a pair)
+    // block sums: wave w loads block w >> 1 of tile rows 64 (w & 1) + lane
+    const float* csrc;
     {
-        const int r = tid & (MT - 1);
+        const int r = 64 * (wave & 1) + lane;
         const int p = base + min(r, cnt - 1);
         const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
-        coff = (uint32_t)(arow * nb) + (uint32_t)(tid >> 7);
+        csrc = csum + arow * nb + (wave >> 1);
     }
 
     const int mfa = min(8, (cnt + 15) >> 4);  // valid slot fragments
     const bool active = nfa > 0;
 
-    struct BStage {
-        uint32_t lo[4], hi[4], q1[4];
-    };
-    auto load_b = [&](BStage& S, int j) {
-#pragma unroll
-        for (int nf = 0; nf < 4; ++nf) {
-            const uint8_t* wp = We + woff[nf] + (uint32_t)j * 36u;
-            const u32x2a4 v = *(const u32x2a4*)wp;  // qs0 bytes 4g-2 .. 4g+5 (d0 in lane g=0)
-            S.lo[nf] = v.x;
-            S.hi[nf] = v.y;                          // lane g=3: bytes 16..19, d1 in the top half
-            S.q1[nf] = *(const uint32_t*)(wp + 20);  // qs1 bytes 4g .. 4g+3
-        }
-    };
-
     // The main loop and epilogue for MF slot fragments (16 slots each).  A tile
     // of at most 32 (64) slots (an expert's last, partial tile, or a small
-    // expert) runs with MF = 2 (4): a quarter (half) of the activation staging,
-    // MFMAs and scale FMAs of a full tile.  Such a tile has too little work per
-    // block pair to hide a memory latency behind it, so it keeps P pairs of
-    // loads in flight (register rings of P stages) instead of one.
-    auto run = [&](auto mf_const, auto p_const) {
+    // expert) runs with MF = 2 (4): a quarter (half) of the activation loads,
+    // MFMAs and scale FMAs of a full tile.
+    auto run = [&](auto mf_const) {
         constexpr int MF = decltype(mf_const)::value;
-        constexpr int P = decltype(p_const)::value;
-        constexpr int NA = MF / 2;  // activation chunks per thread per pair (32 rows each)
+        constexpr int NA = MF / 2;  // activation loads per wave per pair
         f32x4 acc[MF][4];
 #pragma unroll
         for (int i = 0; i < MF; ++i)
 #pragma unroll
             for (int jn = 0; jn < 4; ++jn) acc[i][jn] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-        struct AStage {
-            u32x4a4 a[NA];
-            float c;
-        };
-        auto load_a = [&](AStage& S, int j) {
+        // activation loads: the WG's 2 MF instructions t = NA w + i cover block
+        // t / MF, rows 16 (t % MF) .. +15; lane: row + (lane >> 2), LDS chunk
+        // position lane & 3 holding the row's chunk (lane & 3) ^ ((row >> 2) & 3)
+        const uint16_t* asrc[NA];
+        int adst[NA];
 #pragma unroll
-            for (int i = 0; i < NA; ++i) S.a[i] = *(const u32x4a4*)(act + aoff[i] + (uint32_t)j * 64u);
-            S.c = csum[coff + 2u * (uint32_t)j];
-        };
-        auto store_a = [&](const AStage& S, int slot) {
-            uint8_t* A_lds = smem + slot * SLOT_BYTES;
-            float* C_lds = (float*)(A_lds + 2 * MT * ROWB);
+        for (int i = 0; i < NA; ++i) {
+            const int t = NA * wave + i, blk = t / MF, rg = t % MF;
+            const int r = 16 * rg + (lane >> 2);
+            const int p = base + min(r, cnt - 1);
+            const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
+            const int chunk = (lane & 3) ^ ((r >> 2) & 3);
+            asrc[i] = act + arow * nb * 32 + blk * 32 + 8 * chunk;
+            adst[i] = blk * MT * 64 + rg * 1024;
+        }
+        auto issue = [&](const StageRef& S, int j) {
 #pragma unroll
             for (int i = 0; i < NA; ++i)
-                *(u32x4*)(A_lds + ((ch >> 2) * MT + srow + 32 * i) * ROWB + 16 * (ch & 3)) =
-                    (u32x4){S.a[i].x, S.a[i].y, S.a[i].z, S.a[i].w};
-            C_lds[tid] = S.c;  // block tid >> 7, row tid & 127
+                __builtin_amdgcn_global_load_lds((glb_void_t*)(asrc[i] + 64 * j),
+                                                 (lds_void_t*)(S.a + adst[i]), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void_t*)(csrc + 2 * j),
+                                             (lds_void_t*)(S.c + 64 * wave), 4, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+                __builtin_amdgcn_global_load_lds((glb_void_t*)(We + woff[i] + 36u * (uint32_t)j),
+                                                 (lds_void_t*)(S.w + 64 * 48 * wave + 1024 * i), 16,
+                                                 0, 0);
         };
-        auto compute = [&](int slot, const BStage& S) {
-            const uint8_t* A_lds = smem + slot * SLOT_BYTES;
-            const float* C_lds = (const float*)(A_lds + 2 * MT * ROWB);
+        const int swz = 16 * (g ^ ((l16 >> 2) & 3));  // this lane's chunk position in a row
+        const int q1off = g < 3 ? 20 + 4 * g : 44;     // qs1 dword g in a row's 48 bytes
+        auto compute = [&](const StageRef& S) {
+            const uint8_t* WL = S.w + (wave * 64 + l16) * 48;
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk) {
-                // this block's weights: unpack the lane's qs dword, fetch the scale of
-                // its row from the lane of group 0 (block 0) or group 3 (block 1)
+                // this block's weights: the scale and the lane's qs dword (block 0:
+                // bytes 2 + 4g .. 5 + 4g of the pair, two dwords and an alignbyte;
+                // block 1: bytes 20 + 4g .. 23 + 4g)
                 float dv[4];
                 u32x4 bq[4];
 #pragma unroll
                 for (int nf = 0; nf < 4; ++nf) {
+                    const uint8_t* rp = WL + nf * 16 * 48;
                     if (blk == 0) {
-                        const uint32_t d0 = (uint32_t)__shfl((int)S.lo[nf], l16);
-                        dv[nf] = f16_bits_to_f32(d0 & 0xFFFFu);
-                        bq[nf] = dq_group(__builtin_amdgcn_alignbyte(S.hi[nf], S.lo[nf], 2));
+                        const uint32_t lo = *(const uint32_t*)(rp + 4 * g);
+                        const uint32_t hi = *(const uint32_t*)(rp + 4 * g + 4);
+                        dv[nf] = f16_bits_to_f32(*(const uint16_t*)rp);
+                        bq[nf] = dq_group(__builtin_amdgcn_alignbyte(hi, lo, 2));
                     } else {
-                        const uint32_t d1 = (uint32_t)__shfl((int)S.hi[nf], 48 + l16);
-                        dv[nf] = f16_bits_to_f32(d1 >> 16);
-                        bq[nf] = dq_group(S.q1[nf]);
+                        dv[nf] = f16_bits_to_f32(*(const uint16_t*)(rp + 18));
+                        bq[nf] = dq_group(*(const uint32_t*)(rp + q1off));
                     }
                     // keep the scale a plain fp32 register: otherwise the compiler folds
                     // the fp16 conversion into v_fma_mix_f32 for every scale FMA, which
@@ -290,9 +315,9 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                 // serialise the schedule
 #pragma unroll
                 for (int mf = 0; mf < MF; ++mf) {
-                    const int r = blk * MT + mf * 16;
-                    const u32x4 a = *(const u32x4*)(A_lds + (r + l16) * ROWB + 16 * g);
-                    const f32x4 c = *(const f32x4*)&C_lds[r + 4 * g];
+                    const u32x4 a =
+                        *(const u32x4*)(S.a + blk * MT * 64 + (mf * 16 + l16) * 64 + swz);
+                    const f32x4 c = *(const f32x4*)&S.c[blk * MT + mf * 16 + 4 * g];
                     f32x4 t[4];
 #pragma unroll
                     for (int nf = 0; nf < 4; ++nf) t[nf] = mfma_bf16(a, bq[nf], c);
@@ -303,47 +328,24 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                 }
             }
         };
+        // one iteration: issue pair j + 2 into the stage pair j - 1 used, compute
+        // pair j, wait for this wave's loads of pair j + 1, barrier
+        auto step = [&](const StageRef& cur, const StageRef& nxt, int j) {
+            issue(nxt, min(j + 1, npairs - 1));
+            if (active && j < npairs) compute(cur);
+            wait_vmcnt<0>();
+            stage_barrier();
+        };
 
-        if constexpr (P == 1) {
-            AStage RA;
-            BStage RB;
-            load_a(RA, 0);
-            load_b(RB, 0);
-            store_a(RA, 0);
-            load_a(RA, min(1, npairs - 1));
-            lds_barrier();
-            for (int j = 0; j < npairs; ++j) {
-                store_a(RA, (j + 1) & 1);
-                load_a(RA, min(j + 2, npairs - 1));
-                if (active) compute(j & 1, RB);
-                load_b(RB, min(j + 1, npairs - 1));
-                lds_barrier();
-            }
-        } else {
-            // at the start of pair j: LDS slot j & 1 holds pair j, RA[(j + 1) % P]
-            // pair j + 1, RB[j % P] pair j.  The pairs are run in groups of P (the
-            // ring index a constant); the ones past the end only load and store.
-            AStage RA[P];
-            BStage RB[P];
-            load_a(RA[0], 0);
-            store_a(RA[0], 0);
-#pragma unroll
-            for (int q = 1; q <= P; ++q) load_a(RA[q % P], min(q, npairs - 1));
-#pragma unroll
-            for (int q = 0; q < P; ++q) load_b(RB[q], min(q, npairs - 1));
-            lds_barrier();
-            for (int j0 = 0; j0 < npairs; j0 += P) {
-#pragma unroll
-                for (int u = 0; u < P; ++u) {
-                    const int j = j0 + u;
-                    store_a(RA[(u + 1) % P], (j + 1) & 1);
-                    load_a(RA[(u + 1) % P], min(j + 1 + P, npairs - 1));
-                    if (active && j < npairs) compute(j & 1, RB[u]);
-                    load_b(RB[u], min(j + P, npairs - 1));
-                    lds_barrier();
-                }
-            }
+        issue(st0, 0);
+        wait_vmcnt<0>();
+        stage_barrier();
+        for (int j = 0; j < npairs; j += 2) {
+            step(st0, st1, j);
+            step(st1, st0, j + 1);
         }
+        // the last (clamped) loads land before the workgroup's LDS is released
+        wait_vmcnt<0>();
 
         if (!active) return;
         if (MODE == 0) {
@@ -396,11 +398,11 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         }
     };
     if (cnt <= 32)
-        run(std::integral_constant<int, 2>{}, std::integral_constant<int, LIGHT_DEPTH>{});
+        run(std::integral_constant<int, 2>{});
     else if (cnt <= 64)
-        run(std::integral_constant<int, 4>{}, std::integral_constant<int, LIGHT_DEPTH>{});
+        run(std::integral_constant<int, 4>{});
     else
-        run(std::integral_constant<int, 8>{}, std::integral_constant<int, 1>{});
+        run(std::integral_constant<int, 8>{});
 }
 
 // Activations -> MFMA block order, plus -1.5 * block sums.  One thread per
@@ -470,13 +472,13 @@ hipError_t launch_ffn_mfma(const void* x, int64_t T, int H, const uint8_t* w_gat
     {
         const int n_tiles = (I + NT / 2 - 1) / (NT / 2);
         const int total = (mtiles * n_tiles + 7) / 8 * 8;
-        ffn_mfma<0><<<total, 256, LDS_BYTES, st>>>(xp, xs, w_gate_up, H / 32, 2 * I, I, n_tiles,
+        ffn_mfma<0><<<total, 256, 0, st>>>(xp, xs, w_gate_up, H / 32, 2 * I, I, n_tiles,
                                                    offsets, sorted_slots, K, E, hp, hs, nullptr);
     }
     {
         const int n_tiles = (H + NT - 1) / NT;
         const int total = (mtiles * n_tiles + 7) / 8 * 8;
-        ffn_mfma<1><<<total, 256, LDS_BYTES, st>>>(hp, hs, w_down, I / 32, H, H, n_tiles, offsets,
+        ffn_mfma<1><<<total, 256, 0, st>>>(hp, hs, w_down, I / 32, H, H, n_tiles, offsets,
                                                    sorted_slots, K, E, nullptr, nullptr, y_sorted);
     }
     return hipGetLastError();
@@ -496,7 +498,7 @@ hipError_t launch_linear_mfma(const void* x, int64_t T, int H, const uint8_t* W,
     const int N = (int)T, mtiles = N / MT + 1;
     const int n_tiles = (R + NT - 1) / NT;
     const int total = (mtiles * n_tiles + 7) / 8 * 8;
-    ffn_mfma<1><<<total, 256, LDS_BYTES, st>>>(xp, xs, W, H / 32, R, R, n_tiles, offsets, slots, 1,
+    ffn_mfma<1><<<total, 256, 0, st>>>(xp, xs, W, H / 32, R, R, n_tiles, offsets, slots, 1,
                                                1, nullptr, nullptr, y);
     return hipGetLastError();
 }
