@@ -71,8 +71,8 @@ MOE_DEV int perm_pos(int j) {
 // One qs dword (bytes 4g..4g+3 of a block: nibbles n0..n7 from bit 0 up, n0 =
 // element 4g, n1 = element 4g+16, n2 = element 4g+1, ...) -> four bf16 pairs
 // holding 1 + q/16 for (n0,n4), (n1,n5), (n2,n6), (n3,n7).
-MOE_DEV u32x4 dq_group(uint32_t w) {
-    const uint32_t M = 0x00780078u, ONE = 0x3F803F80u;
+MOE_DEV u32x4 dq_group(uint32_t w, uint32_t M) {
+    const uint32_t ONE = 0x3F803F80u;
     u32x4 r;
     r.x = ((w << 3) & M) | ONE;
     r.y = ((w >> 1) & M) | ONE;
@@ -284,6 +284,10 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         };
         const int swz = 16 * (g ^ ((l16 >> 2) & 3));  // this lane's chunk position in a row
         const int q1off = g < 3 ? 20 + 4 * g : 44;     // qs1 dword g in a row's 48 bytes
+        // the nibble mask in a VGPR: each unpacking step is then a shift and a
+        // v_and_or_b32 (a VOP3 operation takes no literal on gfx950)
+        uint32_t nib_mask;
+        asm volatile("v_mov_b32 %0, 0x00780078" : "=v"(nib_mask));
         auto compute = [&](const StageRef& S) {
             const uint8_t* WL = S.w + (wave * 64 + l16) * 48;
 #pragma unroll
@@ -300,10 +304,10 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                         const uint32_t lo = *(const uint32_t*)(rp + 4 * g);
                         const uint32_t hi = *(const uint32_t*)(rp + 4 * g + 4);
                         dv[nf] = f16_bits_to_f32(*(const uint16_t*)rp);
-                        bq[nf] = dq_group(__builtin_amdgcn_alignbyte(hi, lo, 2));
+                        bq[nf] = dq_group(__builtin_amdgcn_alignbyte(hi, lo, 2), nib_mask);
                     } else {
                         dv[nf] = f16_bits_to_f32(*(const uint16_t*)(rp + 18));
-                        bq[nf] = dq_group(*(const uint32_t*)(rp + q1off));
+                        bq[nf] = dq_group(*(const uint32_t*)(rp + q1off), nib_mask);
                     }
                     // keep the scale a plain fp32 register: otherwise the compiler folds
                     // the fp16 conversion into v_fma_mix_f32 for every scale FMA, which
