@@ -38,6 +38,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int MT = 128;        // slots per tile
 constexpr int NT = 256;        // weight rows per tile (64 per wave)
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
@@ -171,7 +172,8 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
 // each), one 4-byte load of block sums (64 rows of one block) and three
 // 16-byte loads of weights (21 rows per instruction), in place of eight
 // per-lane weight loads that each touched 16 rows.  A third weight stage (two
-// pairs in flight) measured no faster.
+// pairs in flight) measured no faster for full tiles; tiles of at most 32
+// slots, which have a quarter of the work per pair, run a three-stage ring.
 template <int MODE>
 __global__ __launch_bounds__(256) void ffn_mfma(
     const uint16_t* __restrict__ act, const float* __restrict__ csum, const uint8_t* __restrict__ W,
@@ -181,6 +183,10 @@ __global__ __launch_bounds__(256) void ffn_mfma(
     __shared__ __attribute__((aligned(16))) uint8_t a0[2 * MT * 64], a1[2 * MT * 64];
     __shared__ __attribute__((aligned(16))) float cc0[2 * MT], cc1[2 * MT];
     __shared__ __attribute__((aligned(16))) uint8_t w0[NT * 48], w1[NT * 48];
+    // third stage of the light ring (tiles of at most 32 slots)
+    __shared__ __attribute__((aligned(16))) uint8_t la2[2 * 32 * 64];
+    __shared__ __attribute__((aligned(16))) float lc2[2 * 32];
+    __shared__ __attribute__((aligned(16))) uint8_t w2[NT * 48];
     struct StageRef {
         uint8_t* a;
         float* c;
@@ -248,6 +254,8 @@ __global__ __launch_bounds__(256) void ffn_mfma(
     auto run = [&](auto mf_const) {
         constexpr int MF = decltype(mf_const)::value;
         constexpr int NA = MF / 2;  // activation loads per wave per pair
+        constexpr bool LIGHT = MF == 2;
+        constexpr int AROWS = LIGHT ? 32 : MT;  // rows per block in a stage
         f32x4 acc[MF][4];
 #pragma unroll
         for (int i = 0; i < MF; ++i)
@@ -267,15 +275,28 @@ __global__ __launch_bounds__(256) void ffn_mfma(
             const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
             const int chunk = (lane & 3) ^ ((r >> 2) & 3);
             asrc[i] = act + arow * nb * 32 + blk * 32 + 8 * chunk;
-            adst[i] = blk * MT * 64 + rg * 1024;
+            adst[i] = blk * AROWS * 64 + rg * 1024;
+        }
+        // block sums: a heavy stage takes block w >> 1 of rows 64 (w & 1) + lane
+        // from wave w; a light stage its 2 x 32 sums (block lane >> 5, row
+        // lane & 31) from every wave alike (the same bytes, so the four copies
+        // agree)
+        const float* cs = csrc;
+        int cdst = 64 * wave;
+        if constexpr (LIGHT) {
+            const int r = lane & 31;
+            const int p = base + min(r, cnt - 1);
+            const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
+            cs = csum + arow * nb + (lane >> 5);
+            cdst = 0;
         }
         auto issue = [&](const StageRef& S, int j) {
 #pragma unroll
             for (int i = 0; i < NA; ++i)
                 __builtin_amdgcn_global_load_lds((glb_void_t*)(asrc[i] + 64 * j),
                                                  (lds_void_t*)(S.a + adst[i]), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((glb_void_t*)(csrc + 2 * j),
-                                             (lds_void_t*)(S.c + 64 * wave), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void_t*)(cs + 2 * j),
+                                             (lds_void_t*)(S.c + cdst), 4, 0, 0);
 #pragma unroll
             for (int i = 0; i < 3; ++i)
                 __builtin_amdgcn_global_load_lds((glb_void_t*)(We + woff[i] + 36u * (uint32_t)j),
@@ -320,8 +341,8 @@ __global__ __launch_bounds__(256) void ffn_mfma(
 #pragma unroll
                 for (int mf = 0; mf < MF; ++mf) {
                     const u32x4 a =
-                        *(const u32x4*)(S.a + blk * MT * 64 + (mf * 16 + l16) * 64 + swz);
-                    const f32x4 c = *(const f32x4*)&S.c[blk * MT + mf * 16 + 4 * g];
+                        *(const u32x4*)(S.a + blk * AROWS * 64 + (mf * 16 + l16) * 64 + swz);
+                    const f32x4 c = *(const f32x4*)&S.c[blk * AROWS + mf * 16 + 4 * g];
                     f32x4 t[4];
 #pragma unroll
                     for (int nf = 0; nf < 4; ++nf) t[nf] = mfma_bf16(a, bq[nf], c);
@@ -334,19 +355,43 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         };
         // one iteration: issue pair j + 2 into the stage pair j - 1 used, compute
         // pair j, wait for this wave's loads of pair j + 1, barrier
-        auto step = [&](const StageRef& cur, const StageRef& nxt, int j) {
-            issue(nxt, min(j + 1, npairs - 1));
-            if (active && j < npairs) compute(cur);
+        if constexpr (LIGHT) {
+            // three stages (the third in arrays of its own): iteration j issues
+            // pair j+2 into the stage pair j-1 used and waits for pair j+1
+            // (issued an iteration earlier)
+            const StageRef st2{la2, lc2, w2};
+            constexpr int OPS = NA + 4;  // direct loads per wave per pair
+            auto step = [&](const StageRef& cur, const StageRef& nxt, int j) {
+                issue(nxt, min(j + 2, npairs - 1));
+                if (active && j < npairs) compute(cur);
+                wait_vmcnt<OPS>();
+                stage_barrier();
+            };
+            issue(st0, 0);
+            issue(st1, min(1, npairs - 1));
+            wait_vmcnt<OPS>();
+            stage_barrier();
+            for (int j = 0; j < npairs; j += 3) {
+                step(st0, st2, j);
+                step(st1, st0, j + 1);
+                step(st2, st1, j + 2);
+            }
+        } else {
+            // two stages: iteration j issues pair j+1 into the stage pair j-1
+            // used and waits for it before the barrier
+            auto step = [&](const StageRef& cur, const StageRef& nxt, int j) {
+                issue(nxt, min(j + 1, npairs - 1));
+                if (active && j < npairs) compute(cur);
+                wait_vmcnt<0>();
+                stage_barrier();
+            };
+            issue(st0, 0);
             wait_vmcnt<0>();
             stage_barrier();
-        };
-
-        issue(st0, 0);
-        wait_vmcnt<0>();
-        stage_barrier();
-        for (int j = 0; j < npairs; j += 2) {
-            step(st0, st1, j);
-            step(st1, st0, j + 1);
+            for (int j = 0; j < npairs; j += 2) {
+                step(st0, st1, j);
+                step(st1, st0, j + 1);
+            }
         }
         // the last (clamped) loads land before the workgroup's LDS is released
         wait_vmcnt<0>();
