@@ -248,9 +248,9 @@ __global__ __launch_bounds__(256) void ffn_mfma(
     const bool active = nfa > 0;
 
     // The main loop and epilogue for MF slot fragments (16 slots each).  A tile
-    // of at most 32 (64) slots (an expert's last, partial tile, or a small
-    // expert) runs with MF = 2 (4): a quarter (half) of the activation loads,
-    // MFMAs and scale FMAs of a full tile.
+    // of at most 32, 64 or 96 slots (an expert's last, partial tile, or a small
+    // expert) runs with MF = 2, 4 or 6: a quarter, half or three quarters of
+    // the activation loads, MFMAs and scale FMAs of a full tile.
     auto run = [&](auto mf_const) {
         constexpr int MF = decltype(mf_const)::value;
         constexpr int NA = MF / 2;  // activation loads per wave per pair
@@ -450,6 +450,8 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         run(std::integral_constant<int, 2>{});
     else if (cnt <= 64)
         run(std::integral_constant<int, 4>{});
+    else if (cnt <= 96)
+        run(std::integral_constant<int, 6>{});
     else
         run(std::integral_constant<int, 8>{});
 }
