@@ -322,35 +322,46 @@ MOE_DEV void split3(const float (&w)[8], ru32x4& hi, ru32x4& mid, ru32x4& lo) {
     }
 }
 
-template <int NW>
+// tokens from which the bf16 router runs ROUTER_WIDE_TF 16-token fragments per
+// workgroup (each split weight fragment then serves more MFMAs)
+constexpr int ROUTER_WIDE_MIN_T = 2048;
+constexpr int ROUTER_WIDE_TF = 4;
+
+// NW waves split K; TF fragments of 16 tokens per workgroup share each split
+// weight fragment (the split is VALU work, so more token fragments per split
+// means fewer operations per MFMA, at the cost of fewer workgroups).
+template <int NW, int TF>
 __global__ __launch_bounds__(NW * 64) void router_logits_mfma(const uint16_t* __restrict__ x, int T, int H,
                                                           const float* __restrict__ W,
                                                           const float* __restrict__ rsc,
                                                           const float* __restrict__ bias, int E,
                                                           float* __restrict__ logits) {
-    __shared__ f32x4 part[NW - 1][4][64];
+    __shared__ f32x4 part[NW - 1][TF][2][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l16 = lane & 15, g = lane >> 4;
-    const int t0 = blockIdx.x * 32;
+    const int t0 = blockIdx.x * (16 * TF);
     const int e0 = blockIdx.y * 32;
     // this wave's share of H (H is a multiple of 32)
     const int nsteps = H >> 5;
     const int k_begin = (nsteps * wave / NW) * 32, k_end = (nsteps * (wave + 1) / NW) * 32;
-    // A operand: lane (token row l16, k group g); B operand: lane (expert column l16, k group g)
-    const uint16_t* xa = x + (int64_t)min(t0 + l16, T - 1) * H + 8 * g;
-    const uint16_t* xb = x + (int64_t)min(t0 + 16 + l16, T - 1) * H + 8 * g;
+    // A operand: lane (token row l16 of fragment f, k group g); B operand: lane
+    // (expert column l16, k group g)
+    const uint16_t* xf[TF];
+#pragma unroll
+    for (int f = 0; f < TF; ++f) xf[f] = x + (int64_t)min(t0 + 16 * f + l16, T - 1) * H + 8 * g;
     const float* w0 = W + (int64_t)(e0 + l16) * H + 8 * g;
     const float* w1 = W + (int64_t)(e0 + 16 + l16) * H + 8 * g;
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    f32x4 acc2 = {0.f, 0.f, 0.f, 0.f}, acc3 = {0.f, 0.f, 0.f, 0.f};  // second token fragment
+    f32x4 acc[TF][2];
+#pragma unroll
+    for (int f = 0; f < TF; ++f) acc[f][0] = acc[f][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
     // the loads of step k+32 are issued before the MFMAs of step k (clamped at the end)
     struct Step {
-        ru32x4 a, b;
+        ru32x4 a[TF];
         float4 p0, p1, q0, q1, s0, s1;
     };
     auto load = [&](Step& S, int k) {
-        S.a = *(const ru32x4*)(xa + k);
-        S.b = *(const ru32x4*)(xb + k);
+#pragma unroll
+        for (int f = 0; f < TF; ++f) S.a[f] = *(const ru32x4*)(xf[f] + k);
         S.p0 = *(const float4*)(w0 + k);
         S.p1 = *(const float4*)(w0 + k + 4);
         S.q0 = *(const float4*)(w1 + k);
@@ -378,66 +389,77 @@ __global__ __launch_bounds__(NW * 64) void router_logits_mfma(const uint16_t* __
         ru32x4 h0, m0, lo0, h1, m1, lo1;
         split3(wa, h0, m0, lo0);
         split3(wb, h1, m1, lo1);
-        acc0 = rmfma(cur.a, h0, acc0);
-        acc1 = rmfma(cur.a, h1, acc1);
-        acc2 = rmfma(cur.b, h0, acc2);
-        acc3 = rmfma(cur.b, h1, acc3);
-        acc0 = rmfma(cur.a, m0, acc0);
-        acc1 = rmfma(cur.a, m1, acc1);
-        acc2 = rmfma(cur.b, m0, acc2);
-        acc3 = rmfma(cur.b, m1, acc3);
-        acc0 = rmfma(cur.a, lo0, acc0);
-        acc1 = rmfma(cur.a, lo1, acc1);
-        acc2 = rmfma(cur.b, lo0, acc2);
-        acc3 = rmfma(cur.b, lo1, acc3);
+        // hi, then mid, then lo parts: the same per-element order for every tile shape
+#pragma unroll
+        for (int f = 0; f < TF; ++f) {
+            acc[f][0] = rmfma(cur.a[f], h0, acc[f][0]);
+            acc[f][1] = rmfma(cur.a[f], h1, acc[f][1]);
+        }
+#pragma unroll
+        for (int f = 0; f < TF; ++f) {
+            acc[f][0] = rmfma(cur.a[f], m0, acc[f][0]);
+            acc[f][1] = rmfma(cur.a[f], m1, acc[f][1]);
+        }
+#pragma unroll
+        for (int f = 0; f < TF; ++f) {
+            acc[f][0] = rmfma(cur.a[f], lo0, acc[f][0]);
+            acc[f][1] = rmfma(cur.a[f], lo1, acc[f][1]);
+        }
         cur = nxt;
     }
     // partial sums of waves 1..NW-1 to LDS; wave 0 adds them in order and stores
     if (wave > 0) {
-        part[wave - 1][0][lane] = acc0;
-        part[wave - 1][1][lane] = acc1;
-        part[wave - 1][2][lane] = acc2;
-        part[wave - 1][3][lane] = acc3;
+#pragma unroll
+        for (int f = 0; f < TF; ++f) {
+            part[wave - 1][f][0][lane] = acc[f][0];
+            part[wave - 1][f][1][lane] = acc[f][1];
+        }
     }
     __syncthreads();
     if (wave > 0) return;
 #pragma unroll
-    for (int w = 0; w < NW - 1; ++w) {
-        acc0 += part[w][0][lane];
-        acc1 += part[w][1][lane];
-        acc2 += part[w][2][lane];
-        acc3 += part[w][3][lane];
-    }
-    // output lane (token rows 4g..4g+3, expert column l16)
+    for (int w = 0; w < NW - 1; ++w)
+#pragma unroll
+        for (int f = 0; f < TF; ++f) {
+            acc[f][0] += part[w][f][0][lane];
+            acc[f][1] += part[w][f][1][lane];
+        }
+    // output lane (token rows 16 f + 4g .. +3, expert column l16)
     const float b0 = bias ? bias[e0 + l16] : 0.f, b1 = bias ? bias[e0 + 16 + l16] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 4 * g + i;
-        if (t < T) {
-            logits[(int64_t)t * E + e0 + l16] = acc0[i] + b0;
-            logits[(int64_t)t * E + e0 + 16 + l16] = acc1[i] + b1;
+    for (int f = 0; f < TF; ++f)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 16 * f + 4 * g + i;
+            if (t < T) {
+                logits[(int64_t)t * E + e0 + l16] = acc[f][0][i] + b0;
+                logits[(int64_t)t * E + e0 + 16 + l16] = acc[f][1][i] + b1;
+            }
         }
-        if (t + 16 < T) {
-            logits[(int64_t)(t + 16) * E + e0 + l16] = acc2[i] + b0;
-            logits[(int64_t)(t + 16) * E + e0 + 16 + l16] = acc3[i] + b1;
-        }
-    }
 }
 
 hipError_t launch_router_logits(const void* x, int x_dt, int64_t T, int H, const float* W,
                                 const float* rsc, const float* bias, int E, float* logits,
                                 hipStream_t st) {
     if (x_dt == MOE_BF16 && T >= ROUTER_MFMA_MIN_T && E % 32 == 0) {
-        // K split over the 4 waves of a workgroup, over 8 when the tiles are too
-        // few to fill the chip
-        dim3 grid((unsigned)((T + 31) / 32), E / 32);
-        const int64_t wgs = (int64_t)grid.x * grid.y;
-        if (wgs <= 128)
-            router_logits_mfma<8><<<grid, 512, 0, st>>>((const uint16_t*)x, (int)T, H, W, rsc, bias,
-                                                        E, logits);
-        else
-            router_logits_mfma<4><<<grid, 256, 0, st>>>((const uint16_t*)x, (int)T, H, W, rsc, bias,
-                                                        E, logits);
+        // 32 tokens x 32 experts per workgroup, K split over 4 waves (over 8 when
+        // the tiles are too few to fill the chip); many tokens: ROUTER_WIDE_TF
+        // token fragments per workgroup, K over 8 waves
+        const int64_t tiles32 = (T + 31) / 32 * (E / 32);
+        if (T >= ROUTER_WIDE_MIN_T) {
+            constexpr int TF = ROUTER_WIDE_TF;
+            dim3 grid((unsigned)((T + 16 * TF - 1) / (16 * TF)), E / 32);
+            router_logits_mfma<4, TF><<<grid, 256, 0, st>>>((const uint16_t*)x, (int)T, H, W, rsc,
+                                                            bias, E, logits);
+        } else if (tiles32 <= 128) {
+            dim3 grid((unsigned)((T + 31) / 32), E / 32);
+            router_logits_mfma<8, 2><<<grid, 512, 0, st>>>((const uint16_t*)x, (int)T, H, W, rsc,
+                                                           bias, E, logits);
+        } else {
+            dim3 grid((unsigned)((T + 31) / 32), E / 32);
+            router_logits_mfma<4, 2><<<grid, 256, 0, st>>>((const uint16_t*)x, (int)T, H, W, rsc,
+                                                           bias, E, logits);
+        }
     } else if (T < ROUTER_MFMA_MIN_T) {
         dim3 grid(E, (unsigned)((T + ROUTER_GEMV_MAX_T - 1) / ROUTER_GEMV_MAX_T));
         router_variant(x_dt, (int)T, rsc != nullptr, [&](auto xdt, auto tt, auto r) {

@@ -188,3 +188,22 @@ def test_mfma_path_shapes(H, I, E, K, T, zipf):
         assert ((counts > 0) & (counts <= 16)).any() and (counts > 128).any(), counts
     sample = None if H < 1024 else np.arange(0, T, 5)
     _run(L, token_sample=sample)
+
+
+@pytest.mark.parametrize("I", [64, 192])
+def test_mfma_tile_size_boundaries(I):
+    # Injected logits route exactly 1, 32, 33, 64, 65, 96, 97 and 129 slots to
+    # the eight experts: both sides of every slot-tile variant (2, 4, 6 and 8
+    # fragments of 16 slots, and a second tile of one slot).  I = 64 gives the
+    # down product a single block pair, I = 192 an odd number of pairs.
+    counts = [1, 32, 33, 64, 65, 96, 97, 129]
+    T, E = sum(counts), len(counts)
+    spec = synth.LayerSpec("tile-bounds-I%d" % I, H=256, E=E, K=1, I=I, T=T, act="bf16",
+                           router_std=1 / 16, seed=29)
+    L = synth.make_layer(spec)
+    rng = np.random.default_rng(31)
+    owner = rng.permutation(np.repeat(np.arange(E), counts))
+    lg = (rng.standard_normal((T, E)) * 0.1).astype(np.float32)
+    lg[np.arange(T), owner] += 10.0
+    g, res = _run(L, logits_in=lg)
+    assert np.array_equal(np.diff(g["offsets"]), np.array(counts)), np.diff(g["offsets"])
