@@ -105,14 +105,44 @@ MOE_DEV void permute_block(const int32_t* ids, int N, int E, int32_t* offsets,
 // logits go in ascending expert order.  Weights: softmax over the K kept
 // logits.  Every lane of the wave must be active.
 // COH: the logits were written by other workgroups of this launch (coherent loads).
+// (all four loads unconditional, clamped to expert E-1, so that they are in
+// flight together; a load in a branch waits for itself)
 template <bool COH = false>
 MOE_DEV void topk_load(const float* l, int E, float (&v)[4]) {
     const int lane = threadIdx.x & 63;
+    float r[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = e < E ? (COH ? coherent_load(l + e) : l[e]) : 0.f;
+        const int e = min(lane + 64 * i, E - 1);
+        r[i] = COH ? coherent_load(l + e) : l[e];
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = lane + 64 * i < E ? r[i] : 0.f;
+}
+
+// Order-preserving map of a float to an int key (v + 0 has turned -0 into +0):
+// the rounds below compare keys with integer max, which the DPP steps take as
+// one instruction each (a float max canonicalises its inputs first).  NaN ranks
+// below every number, as under fmaxf; a taken or absent expert is INT_MIN.
+MOE_DEV int topk_key(float v) {
+    const int b = __float_as_int(v);
+    return v != v ? INT_MIN + 1 : (b ^ ((b >> 31) & 0x7FFFFFFF));
+}
+MOE_DEV float topk_unkey(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
+
+template <int CTRL, int ROW_MASK = 0xF>
+MOE_DEV int dpp_i32(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+MOE_DEV int wave_max_i32(int v) {
+    v = max(v, dpp_i32<DPP_QUAD_XOR1>(v, v));
+    v = max(v, dpp_i32<DPP_QUAD_XOR2>(v, v));
+    v = max(v, dpp_i32<DPP_ROW_HALF_MIRROR>(v, v));
+    v = max(v, dpp_i32<DPP_ROW_MIRROR>(v, v));
+    v = max(v, dpp_i32<DPP_ROW_BCAST15, 0xA>(INT_MIN, v));
+    v = max(v, dpp_i32<DPP_ROW_BCAST31, 0xC>(INT_MIN, v));
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
 // NT tokens at once (one wave): the K rounds of the tokens are interleaved so
@@ -122,15 +152,12 @@ template <int NT>
 MOE_DEV void topk_select_n(const float (&lv)[NT][4], int E, int K, int32_t* const (&ids)[NT],
                            float* const (&w)[NT]) {
     const int lane = threadIdx.x & 63;
-    float v[NT][4];
-    bool live[NT][4];
+    int key[NT][4];
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            live[n][i] = lane + 64 * i < E;
-            v[n][i] = live[n][i] ? lv[n][i] + 0.f : -INFINITY;  // + 0 turns -0 into +0
-        }
+        for (int i = 0; i < 4; ++i)
+            key[n][i] = lane + 64 * i < E ? topk_key(lv[n][i] + 0.f) : INT_MIN;
     float selv[NT][MOE_MAX_K];
     int seli[NT][MOE_MAX_K];
 #pragma unroll
@@ -141,31 +168,26 @@ MOE_DEV void topk_select_n(const float (&lv)[NT][4], int E, int K, int32_t* cons
             seli[n][k] = 0;
         }
         if (k < K) {
-            float m[NT];
+            int m[NT];
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+                m[n] = wave_max_i32(max(max(key[n][0], key[n][1]), max(key[n][2], key[n][3])));
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
-                m[n] = -INFINITY;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (live[n][i]) m[n] = fmaxf(m[n], v[n][i]);
-            }
-#pragma unroll
-            for (int n = 0; n < NT; ++n) m[n] = wave_max(m[n]);
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
+                // the lowest expert index holding the maximum
                 int idx = -1;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const uint64_t bal = __ballot(live[n][i] && v[n][i] == m[n]);
+                    const uint64_t bal = __ballot(key[n][i] == m[n]);
                     if (idx < 0 && bal) idx = 64 * i + (int)__builtin_ctzll(bal);
                 }
-                if (idx < 0) idx = 0;  // only when every remaining logit is NaN
-                selv[n][k] = m[n];
+                if (idx < 0) idx = 0;  // not reached: the maximum is some lane's key
+                selv[n][k] = topk_unkey(m[n]);
                 seli[n][k] = idx;
                 if ((idx & 63) == lane) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (i == (idx >> 6)) live[n][i] = false;
+                        if (i == (idx >> 6)) key[n][i] = INT_MIN;
                 }
             }
         }
