@@ -12,6 +12,13 @@
 namespace moe {
 
 // One tile: a single workgroup sorts every slot.
+__global__ __launch_bounds__(64) void permute_one_wave(const int32_t* __restrict__ ids, int N, int E,
+                                                      int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ sorted_slots,
+                                                      int32_t* __restrict__ slot_pos) {
+    permute_wave(ids, N, E, offsets, sorted_slots, slot_pos);
+}
+
 __global__ __launch_bounds__(256) void permute_single(const int32_t* __restrict__ ids, int N, int E,
                                                       int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ sorted_slots,
@@ -199,6 +206,10 @@ size_t permute_ws_bytes(int64_t N, int E) {
 
 hipError_t launch_permute(const int32_t* ids, int N, int E, int32_t* offsets, int32_t* sorted_slots,
                           int32_t* slot_pos, void* ws, hipStream_t st) {
+    if (N <= PERM_WAVE) {
+        permute_one_wave<<<1, 64, 0, st>>>(ids, N, E, offsets, sorted_slots, slot_pos);
+        return hipGetLastError();
+    }
     if (N <= PERM_TILE) {
         permute_single<<<1, 256, 0, st>>>(ids, N, E, offsets, sorted_slots, slot_pos);
         return hipGetLastError();

@@ -99,6 +99,56 @@ MOE_DEV void permute_block(const int32_t* ids, int N, int E, int32_t* offsets,
     }
 }
 
+// The same sort for N <= 64 slots by one wave (the caller's wave 0 alone; no
+// workgroup barrier): an LDS histogram of the expert ids, an exclusive scan of
+// it across the wave (lane l holds experts 4l .. 4l+3), and the stable rank of
+// each slot among the slots of its expert from the wave match.
+constexpr int PERM_WAVE = 64;
+
+MOE_DEV void permute_wave(const int32_t* ids, int N, int E, int32_t* offsets,
+                          int32_t* sorted_slots, int32_t* slot_pos) {
+    __shared__ int hcnt[MOE_MAX_E];
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hcnt[4 * lane + i] = 0;
+    const bool valid = lane < N;
+    const int e = valid ? ids[lane] : 0;
+    __builtin_amdgcn_wave_barrier();
+    if (valid) atomicAdd(&hcnt[e], 1);
+    __builtin_amdgcn_wave_barrier();
+    int c[4], tot = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        c[i] = 4 * lane + i < E ? hcnt[4 * lane + i] : 0;
+        tot += c[i];
+    }
+    int incl = tot;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
+    }
+    int run = incl - tot;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ex = 4 * lane + i;
+        if (ex < E) {
+            offsets[ex] = run;
+            hcnt[ex] = run;  // now the exclusive offsets
+        }
+        if (ex == E - 1) offsets[E] = run + c[i];
+        run += c[i];
+    }
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t m = match_key9(valid ? (uint32_t)e : 256u);
+    if (valid) {
+        const int pos = hcnt[e] + __popcll(m & lanemask_lt());
+        sorted_slots[pos] = lane;
+        slot_pos[lane] = pos;
+    }
+}
+
 // Top-K of one token's E logits by one wave; lane l holds experts l, l+64,
 // l+128, l+192.  Each of the K rounds takes the wave maximum (DPP) of the
 // untaken logits and the lowest expert index holding it (ballots), so equal

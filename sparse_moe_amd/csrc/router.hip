@@ -248,7 +248,11 @@ __global__ __launch_bounds__(256) void route_small(const void* __restrict__ x, i
         topk_select(v, E, K, ids + t0 * K, w + t0 * K);
     }
     __syncthreads();  // ids of every token are written
-    permute_block(ids, T * K, E, offsets, sorted_slots, slot_pos);
+    if (T * K <= PERM_WAVE) {
+        if (wave == 0) permute_wave(ids, T * K, E, offsets, sorted_slots, slot_pos);
+    } else {
+        permute_block(ids, T * K, E, offsets, sorted_slots, slot_pos);
+    }
     if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
