@@ -147,15 +147,24 @@ __global__ __launch_bounds__(256) void permute_tiles(const int32_t* __restrict__
     if (tid < E) tile_counts[(int64_t)blockIdx.x * E + tid] = run[tid];
 }
 
-// One workgroup: per-expert prefix over tiles (tile_base), then expert offsets.
-__global__ __launch_bounds__(256) void permute_scan(int ntiles, int E,
-                                                    const int32_t* __restrict__ tile_counts,
-                                                    int32_t* __restrict__ tile_base,
-                                                    int32_t* __restrict__ offsets) {
+// Scatter, with the scan folded in: every workgroup sums the per-expert tile
+// counts itself (its tile's base is the sum over the earlier tiles; the expert
+// offsets, a scan of the totals, are the same in every workgroup and the first
+// one stores them), which saves the launch of a one-workgroup scan.
+__global__ __launch_bounds__(256) void permute_scatter(const int32_t* __restrict__ ids, int N, int E,
+                                                       int ntiles,
+                                                       const int32_t* __restrict__ tile_counts,
+                                                       const int32_t* __restrict__ local_rank,
+                                                       int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ sorted_slots,
+                                                       int32_t* __restrict__ slot_pos) {
+    __shared__ int tb[MOE_MAX_E];
     __shared__ int tot[256];
     __shared__ int tmp[256];
+    __shared__ int off[MOE_MAX_E + 1];
     const int e = threadIdx.x;
-    int run = 0;
+    const int me = blockIdx.x;
+    int before = 0, all = 0;
     if (e < E) {
         int tile = 0;
         for (; tile + 8 <= ntiles; tile += 8) {
@@ -164,34 +173,27 @@ __global__ __launch_bounds__(256) void permute_scan(int ntiles, int E,
             for (int i = 0; i < 8; ++i) c[i] = tile_counts[(int64_t)(tile + i) * E + e];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                tile_base[(int64_t)(tile + i) * E + e] = run;
-                run += c[i];
+                before += tile + i < me ? c[i] : 0;
+                all += c[i];
             }
         }
         for (; tile < ntiles; ++tile) {
             const int c = tile_counts[(int64_t)tile * E + e];
-            tile_base[(int64_t)tile * E + e] = run;
-            run += c;
+            before += tile < me ? c : 0;
+            all += c;
         }
+        tb[e] = before;
     }
-    tot[e] = run;
+    tot[e] = all;
     __syncthreads();
-    block_exclusive_scan256(tot, E, tmp, offsets, nullptr);
-}
-
-__global__ __launch_bounds__(256) void permute_scatter(const int32_t* __restrict__ ids, int N, int E,
-                                                       const int32_t* __restrict__ tile_base,
-                                                       const int32_t* __restrict__ local_rank,
-                                                       const int32_t* __restrict__ offsets,
-                                                       int32_t* __restrict__ sorted_slots,
-                                                       int32_t* __restrict__ slot_pos) {
-    const int base = blockIdx.x * PERM_TILE;
+    block_exclusive_scan256(tot, E, tmp, me == 0 ? offsets : nullptr, off);
+    const int base = me * PERM_TILE;
 #pragma unroll
     for (int r = 0; r < PERM_TILE / 256; ++r) {
         const int s = base + r * 256 + threadIdx.x;
         if (s < N) {
-            const int e = ids[s];
-            const int pos = offsets[e] + tile_base[(int64_t)blockIdx.x * E + e] + local_rank[s];
+            const int ex = ids[s];
+            const int pos = off[ex] + tb[ex] + local_rank[s];
             sorted_slots[pos] = s;
             slot_pos[s] = pos;
         }
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(256) void permute_scatter(const int32_t* __restrict
 size_t permute_ws_bytes(int64_t N, int E) {
     if (N <= PERM_WIDE) return 0;
     const int64_t ntiles = (N + PERM_TILE - 1) / PERM_TILE;
-    return (size_t)(2 * ntiles * E + N) * sizeof(int32_t);
+    return (size_t)(ntiles * E + N) * sizeof(int32_t);
 }
 
 hipError_t launch_permute(const int32_t* ids, int N, int E, int32_t* offsets, int32_t* sorted_slots,
@@ -220,12 +222,10 @@ hipError_t launch_permute(const int32_t* ids, int N, int E, int32_t* offsets, in
     }
     const int ntiles = (N + PERM_TILE - 1) / PERM_TILE;
     int32_t* tile_counts = (int32_t*)ws;
-    int32_t* tile_base = tile_counts + (int64_t)ntiles * E;
-    int32_t* local_rank = tile_base + (int64_t)ntiles * E;
+    int32_t* local_rank = tile_counts + (int64_t)ntiles * E;
     permute_tiles<<<ntiles, 256, 0, st>>>(ids, N, E, tile_counts, local_rank);
-    permute_scan<<<1, 256, 0, st>>>(ntiles, E, tile_counts, tile_base, offsets);
-    permute_scatter<<<ntiles, 256, 0, st>>>(ids, N, E, tile_base, local_rank, offsets, sorted_slots,
-                                            slot_pos);
+    permute_scatter<<<ntiles, 256, 0, st>>>(ids, N, E, ntiles, tile_counts, local_rank, offsets,
+                                            sorted_slots, slot_pos);
     return hipGetLastError();
 }
 

@@ -65,7 +65,7 @@ def test_permute_validation_and_workspace():
     f = lib.moe_permute
     assert lib.moe_permute_workspace_bytes(4, 2, 8) == 0           # one tile: no workspace
     big = lib.moe_permute_workspace_bytes(4096, 8, 128)
-    assert big >= (2 * 32 * 128 + 32768) * 4 and big % 256 == 0
+    assert big >= (32 * 128 + 32768) * 4 and big % 256 == 0
     assert f(A, 4096, 8, 128, A, A, A, None, 0, None) == WS
     assert f(A, 4096, 8, 128, A, A, A, A, 16, None) == WS
     assert f(A, 4, 2, 8, None, A, A, None, 0, None) == NULL
