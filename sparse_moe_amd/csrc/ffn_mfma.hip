@@ -456,40 +456,49 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         run(std::integral_constant<int, 8>{});
 }
 
-// Activations -> MFMA block order, plus -1.5 * block sums.  One thread per
-// (token, block).
+// Activations -> MFMA block order, plus -1.5 * block sums.  Four lanes per
+// 32-element block, one 16-byte quarter each (loads and stores of a wave are
+// contiguous): output chunk c of a block holds elements 4c..4c+3 of quarter
+// c >> 1 and elements 4c+16..4c+19 of quarter (c >> 1) + 2, which reach lane
+// c through quad DPP moves.  The block sum is each lane's 8 values in order,
+// then the quad's four partial sums.
 __global__ __launch_bounds__(256) void ffn_mfma_prep(const uint16_t* __restrict__ x, int64_t nblocks,
                                                      uint16_t* __restrict__ xp,
                                                      float* __restrict__ xs) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= nblocks) return;
-    const u32x4* src = (const u32x4*)(x + i * 32);
-    uint32_t v[16];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const u32x4 t = src[c];
-        v[4 * c] = t.x; v[4 * c + 1] = t.y; v[4 * c + 2] = t.z; v[4 * c + 3] = t.w;
-    }
-    uint16_t e[32], o[32];
+    const int64_t nq = nblocks * 4;
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const u32x4 v = reinterpret_cast<const u32x4*>(x)[min(q, nq - 1)];
+    const int c = threadIdx.x & 3;
     float s = 0.f;
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-        e[j] = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
-        s += bf16_to_f32(e[j]);
+    for (int i = 0; i < 4; ++i) {
+        s += __uint_as_float(w4[i] << 16);
+        s += __uint_as_float(w4[i] & 0xFFFF0000u);
     }
-#pragma unroll
-    for (int j = 0; j < 32; ++j) o[perm_pos(j)] = e[j];
-    u32x4* dst = (u32x4*)(xp + i * 32);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        u32x4 t;
-        t.x = o[8 * c] | ((uint32_t)o[8 * c + 1] << 16);
-        t.y = o[8 * c + 2] | ((uint32_t)o[8 * c + 3] << 16);
-        t.z = o[8 * c + 4] | ((uint32_t)o[8 * c + 5] << 16);
-        t.w = o[8 * c + 6] | ((uint32_t)o[8 * c + 7] << 16);
-        dst[c] = t;
+    s += dpp_f32<DPP_QUAD_XOR1>(s, s);
+    s += dpp_f32<DPP_QUAD_XOR2>(s, s);
+    constexpr int FROM_LO = 0x50;  // quad_perm [0,0,1,1]: lane c reads lane c >> 1
+    constexpr int FROM_HI = 0xFA;  // quad_perm [2,2,3,3]: lane c reads lane (c >> 1) + 2
+    auto mv = [](uint32_t a, auto ctrl) {
+        return (uint32_t)__builtin_amdgcn_update_dpp((int)a, (int)a, decltype(ctrl)::value, 0xF, 0xF, false);
+    };
+    using LO = std::integral_constant<int, FROM_LO>;
+    using HI = std::integral_constant<int, FROM_HI>;
+    const bool odd = c & 1;
+    // A = elements (4c, 4c+1), B = (4c+2, 4c+3), C = (4c+16, 4c+17), D = (4c+18, 4c+19)
+    const uint32_t a0 = mv(v.x, LO{}), b0 = mv(v.y, LO{}), a1 = mv(v.z, LO{}), b1 = mv(v.w, LO{});
+    const uint32_t c0 = mv(v.x, HI{}), d0 = mv(v.y, HI{}), c1 = mv(v.z, HI{}), d1 = mv(v.w, HI{});
+    const uint32_t A = odd ? a1 : a0, B = odd ? b1 : b0, C = odd ? c1 : c0, D = odd ? d1 : d0;
+    u32x4 o;
+    o.x = (A & 0xFFFFu) | (B << 16);
+    o.y = (C & 0xFFFFu) | (D << 16);
+    o.z = (A >> 16) | (B & 0xFFFF0000u);
+    o.w = (C >> 16) | (D & 0xFFFF0000u);
+    if (q < nq) {
+        reinterpret_cast<u32x4*>(xp)[q] = o;
+        if (c == 0) xs[q >> 2] = -1.5f * s;
     }
-    xs[i] = -1.5f * s;
 }
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
@@ -515,7 +524,7 @@ hipError_t launch_ffn_mfma(const void* x, int64_t T, int H, const uint8_t* w_gat
     float* hs = (float*)p;
 
     const int64_t nblk = T * (H / 32);
-    ffn_mfma_prep<<<(unsigned)((nblk + 255) / 256), 256, 0, st>>>((const uint16_t*)x, nblk, xp, xs);
+    ffn_mfma_prep<<<(unsigned)((4 * nblk + 255) / 256), 256, 0, st>>>((const uint16_t*)x, nblk, xp, xs);
 
     // slot tiles: sum over experts of ceil(count / MT) <= N / MT + (experts hit);
     // the workgroups past the real count exit at once
@@ -545,7 +554,7 @@ hipError_t launch_linear_mfma(const void* x, int64_t T, int H, const uint8_t* W,
     uint16_t* xp = (uint16_t*)ws;
     float* xs = (float*)((uint8_t*)ws + align256((size_t)T * H * 2));
     const int64_t nblk = T * (H / 32);
-    ffn_mfma_prep<<<(unsigned)((nblk + 255) / 256), 256, 0, st>>>((const uint16_t*)x, nblk, xp, xs);
+    ffn_mfma_prep<<<(unsigned)((4 * nblk + 255) / 256), 256, 0, st>>>((const uint16_t*)x, nblk, xp, xs);
     const int N = (int)T, mtiles = N / MT + 1;
     const int n_tiles = (R + NT - 1) / NT;
     const int total = (mtiles * n_tiles + 7) / 8 * 8;
