@@ -185,6 +185,16 @@ MOE_DEV int dpp_i32(int old, int v) {
     return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
 }
 
+MOE_DEV int wave_min_i32(int v) {
+    v = min(v, dpp_i32<DPP_QUAD_XOR1>(v, v));
+    v = min(v, dpp_i32<DPP_QUAD_XOR2>(v, v));
+    v = min(v, dpp_i32<DPP_ROW_HALF_MIRROR>(v, v));
+    v = min(v, dpp_i32<DPP_ROW_MIRROR>(v, v));
+    v = min(v, dpp_i32<DPP_ROW_BCAST15, 0xA>(INT_MAX, v));
+    v = min(v, dpp_i32<DPP_ROW_BCAST31, 0xC>(INT_MAX, v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
 MOE_DEV int wave_max_i32(int v) {
     v = max(v, dpp_i32<DPP_QUAD_XOR1>(v, v));
     v = max(v, dpp_i32<DPP_QUAD_XOR2>(v, v));
@@ -218,36 +228,34 @@ MOE_DEV void topk_select_n(const float (&lv)[NT][4], int E, int K, int32_t* cons
             seli[n][k] = 0;
         }
         if (k < K) {
-            int m[NT];
+            // the maximum key, then the lowest expert index holding it: two wave
+            // reductions on the vector unit (no ballot and scalar search)
+            int m[NT], idx[NT];
 #pragma unroll
             for (int n = 0; n < NT; ++n)
                 m[n] = wave_max_i32(max(max(key[n][0], key[n][1]), max(key[n][2], key[n][3])));
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
-                // the lowest expert index holding the maximum
-                int idx = -1;
+                int li = INT_MAX;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint64_t bal = __ballot(key[n][i] == m[n]);
-                    if (idx < 0 && bal) idx = 64 * i + (int)__builtin_ctzll(bal);
-                }
-                if (idx < 0) idx = 0;  // not reached: the maximum is some lane's key
+                for (int i = 0; i < 4; ++i)
+                    li = min(li, key[n][i] == m[n] ? 64 * i + lane : INT_MAX);
+                idx[n] = wave_min_i32(li);
+            }
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
                 selv[n][k] = topk_unkey(m[n]);
-                seli[n][k] = idx;
-                if ((idx & 63) == lane) {
+                seli[n][k] = idx[n];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (i == (idx >> 6)) key[n][i] = INT_MIN;
-                }
+                for (int i = 0; i < 4; ++i)
+                    key[n][i] = 64 * i + lane == idx[n] ? INT_MIN : key[n][i];
             }
         }
     }
+    // softmax over the K kept logits: lane k takes exp(v_k - v_0), the sum is a
+    // 16-lane reduction (K <= 16) in a fixed order
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-        float s = 0.f;
-#pragma unroll
-        for (int k = 0; k < MOE_MAX_K; ++k)
-            if (k < K) s += expf(selv[n][k] - selv[n][0]);
         float myv = 0.f;
         int myi = 0;
 #pragma unroll
@@ -256,9 +264,11 @@ MOE_DEV void topk_select_n(const float (&lv)[NT][4], int E, int K, int32_t* cons
                 myv = selv[n][k];
                 myi = seli[n][k];
             }
+        const float ex = lane < K ? expf(myv - selv[n][0]) : 0.f;
+        const float s = group_sum<16>(ex);
         if (lane < K) {
             ids[n][lane] = myi;
-            w[n][lane] = expf(myv - selv[n][0]) / s;
+            w[n][lane] = ex / s;
         }
     }
 }
