@@ -334,7 +334,7 @@ constexpr int ROUTER_WIDE_TF = 4;
 // NW waves split K; TF fragments of 16 tokens per workgroup share each split
 // weight fragment (the split is VALU work, so more token fragments per split
 // means fewer operations per MFMA, at the cost of fewer workgroups).
-template <int NW, int TF>
+template <int NW, int TF, bool RSC>
 __global__ __launch_bounds__(NW * 64) void router_logits_mfma(const uint16_t* __restrict__ x, int T, int H,
                                                           const float* __restrict__ W,
                                                           const float* __restrict__ rsc,
@@ -361,7 +361,8 @@ __global__ __launch_bounds__(NW * 64) void router_logits_mfma(const uint16_t* __
     // the loads of step k+32 are issued before the MFMAs of step k (clamped at the end)
     struct Step {
         ru32x4 a[TF];
-        float4 p0, p1, q0, q1, s0, s1;
+        float4 p0, p1, q0, q1;
+        float4 s0[RSC ? 1 : 0], s1[RSC ? 1 : 0];
     };
     auto load = [&](Step& S, int k) {
 #pragma unroll
@@ -370,9 +371,9 @@ __global__ __launch_bounds__(NW * 64) void router_logits_mfma(const uint16_t* __
         S.p1 = *(const float4*)(w0 + k + 4);
         S.q0 = *(const float4*)(w1 + k);
         S.q1 = *(const float4*)(w1 + k + 4);
-        if (rsc) {
-            S.s0 = *(const float4*)(rsc + 8 * g + k);
-            S.s1 = *(const float4*)(rsc + 8 * g + k + 4);
+        if constexpr (RSC) {
+            S.s0[0] = *(const float4*)(rsc + 8 * g + k);
+            S.s1[0] = *(const float4*)(rsc + 8 * g + k + 4);
         }
     };
     Step cur, nxt;
@@ -381,9 +382,9 @@ __global__ __launch_bounds__(NW * 64) void router_logits_mfma(const uint16_t* __
         load(nxt, min(k + 32, H - 32));
         float wa[8] = {cur.p0.x, cur.p0.y, cur.p0.z, cur.p0.w, cur.p1.x, cur.p1.y, cur.p1.z, cur.p1.w};
         float wb[8] = {cur.q0.x, cur.q0.y, cur.q0.z, cur.q0.w, cur.q1.x, cur.q1.y, cur.q1.z, cur.q1.w};
-        if (rsc) {
-            const float sv[8] = {cur.s0.x, cur.s0.y, cur.s0.z, cur.s0.w,
-                                 cur.s1.x, cur.s1.y, cur.s1.z, cur.s1.w};
+        if constexpr (RSC) {
+            const float sv[8] = {cur.s0[0].x, cur.s0[0].y, cur.s0[0].z, cur.s0[0].w,
+                                 cur.s1[0].x, cur.s1[0].y, cur.s1[0].z, cur.s1[0].w};
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
                 wa[jj] *= sv[jj];
@@ -421,7 +422,9 @@ __global__ __launch_bounds__(NW * 64) void router_logits_mfma(const uint16_t* __
     }
     __syncthreads();
     if (wave > 0) return;
-#pragma unroll
+    // in wave order (a rolled loop: unrolled, the partial reads of many waves
+    // are all hoisted and the registers run out)
+#pragma unroll 1
     for (int w = 0; w < NW - 1; ++w)
 #pragma unroll
         for (int f = 0; f < TF; ++f) {
@@ -450,20 +453,26 @@ hipError_t launch_router_logits(const void* x, int x_dt, int64_t T, int H, const
         // the tiles are too few to fill the chip); many tokens: ROUTER_WIDE_TF
         // token fragments per workgroup, K over 8 waves
         const int64_t tiles32 = (T + 31) / 32 * (E / 32);
-        if (T >= ROUTER_WIDE_MIN_T) {
-            constexpr int TF = ROUTER_WIDE_TF;
-            dim3 grid((unsigned)((T + 16 * TF - 1) / (16 * TF)), E / 32);
-            router_logits_mfma<4, TF><<<grid, 256, 0, st>>>((const uint16_t*)x, (int)T, H, W, rsc,
-                                                            bias, E, logits);
-        } else if (tiles32 <= 128) {
-            dim3 grid((unsigned)((T + 31) / 32), E / 32);
-            router_logits_mfma<8, 2><<<grid, 512, 0, st>>>((const uint16_t*)x, (int)T, H, W, rsc,
-                                                           bias, E, logits);
-        } else {
-            dim3 grid((unsigned)((T + 31) / 32), E / 32);
-            router_logits_mfma<4, 2><<<grid, 256, 0, st>>>((const uint16_t*)x, (int)T, H, W, rsc,
-                                                           bias, E, logits);
-        }
+        auto go = [&](auto rsc_c) {
+            constexpr bool R = decltype(rsc_c)::value;
+            if (T >= ROUTER_WIDE_MIN_T) {
+                constexpr int TF = ROUTER_WIDE_TF;
+                dim3 grid((unsigned)((T + 16 * TF - 1) / (16 * TF)), E / 32);
+                router_logits_mfma<4, TF, R><<<grid, 256, 0, st>>>((const uint16_t*)x, (int)T, H, W,
+                                                                   rsc, bias, E, logits);
+            } else if (tiles32 <= 128) {
+                // few tiles: 16 tokens per workgroup and K over 16 waves, so that
+                // each wave's chain of dependent K steps is short
+                dim3 grid((unsigned)((T + 15) / 16), E / 32);
+                router_logits_mfma<16, 1, R><<<grid, 1024, 0, st>>>((const uint16_t*)x, (int)T, H, W,
+                                                                    rsc, bias, E, logits);
+            } else {
+                dim3 grid((unsigned)((T + 31) / 32), E / 32);
+                router_logits_mfma<4, 2, R><<<grid, 256, 0, st>>>((const uint16_t*)x, (int)T, H, W,
+                                                                  rsc, bias, E, logits);
+            }
+        };
+        if (rsc) go(std::true_type{}); else go(std::false_type{});
     } else if (T < ROUTER_MFMA_MIN_T) {
         dim3 grid(E, (unsigned)((T + ROUTER_GEMV_MAX_T - 1) / ROUTER_GEMV_MAX_T));
         router_variant(x_dt, (int)T, rsc != nullptr, [&](auto xdt, auto tt, auto r) {
