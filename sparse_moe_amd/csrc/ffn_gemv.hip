@@ -65,17 +65,37 @@ MOE_DEV void digitize_quarter(const float v[8], int m, uint32_t* words, int wstr
     if (amax > 0.f) {
         const float inv = (float)DIGIT_NMAX / amax;
         s = amax / (float)DIGIT_NMAX;
+        uint32_t u[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             int n = (int)rintf(v[j] * inv);
             n = max(-DIGIT_NMAX, min(DIGIT_NMAX, n));
             // n + 0x8888 = sum_k h_k 16^k with hex digits h_k, so n = sum_k (h_k - 8) 16^k:
-            // the balanced digits are h_k - 8, whose 4-bit two's complement is h_k ^ 8.
-            const uint32_t u = (uint32_t)(n + 0x8888) ^ 0x8888u;
-            const int p = ((j & 3) << 1) | (j >> 2);   // nibble of element 4m+(j&3)+16(j>>2)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) wd[k] |= ((u >> (4 * k)) & 15u) << (4 * p);
+            // the balanced digits are h_k - 8, whose 4-bit two's complement is h_k ^ 8
+            // (16 bits: |n| <= DIGIT_NMAX keeps n + 0x8888 below 2^16)
+            u[j] = (uint32_t)(n + 0x8888) ^ 0x8888u;
         }
+        // Word k takes digit k of element j at nibble p(j) = 2 (j & 3) + (j >> 2): a
+        // nibble transpose.  Elements in nibble order pair up as the 16-bit halves of
+        // R_i (nibbles a0..a3 b0..b3), whose nibbles are zipped to a0 b0 a1 b1 .. a3 b3
+        // (a byte swap, then a nibble swap), so byte k of R_i is the pair's digit k;
+        // a 4 x 4 byte transpose of R_0..R_3 then gives the words.
+        uint32_t R[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // nibble positions 2i and 2i+1 hold elements i and i + 4
+            uint32_t x = u[i] | (u[i + 4] << 16);
+            x = __builtin_amdgcn_perm(x, x, 0x03010200u);
+            R[i] = (x & 0xF00FF00Fu) | ((x >> 4) & 0x00F000F0u) | ((x << 4) & 0x0F000F00u);
+        }
+        const uint32_t t0 = __builtin_amdgcn_perm(R[1], R[0], 0x05010400u);
+        const uint32_t t1 = __builtin_amdgcn_perm(R[1], R[0], 0x07030602u);
+        const uint32_t t2 = __builtin_amdgcn_perm(R[3], R[2], 0x05010400u);
+        const uint32_t t3 = __builtin_amdgcn_perm(R[3], R[2], 0x07030602u);
+        wd[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+        wd[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+        wd[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+        wd[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) words[(4 * m + k) * wstride] = wd[k];
