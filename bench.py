@@ -341,8 +341,8 @@ def main():
     if args.summarize_traffic:
         return summarize_traffic(args)
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the layer would shard over experts)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the layer would shard over experts, one process per GPU)", file=sys.stderr)
         sys.exit(2)
     import torch
     from sparse_moe_amd import binding, synth
