@@ -395,13 +395,22 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         }
         // the last (clamped) loads land before the workgroup's LDS is released
         wait_vmcnt<0>();
+        // the epilogues reuse stage arrays: every wave's loads have landed once
+        // all waves pass this barrier
+        stage_barrier();
 
         if (!active) return;
         if (MODE == 0) {
             // h = GELU(g) * u for hidden columns c0 .. c0+31: one Q4_0 block of the
-            // down product's K, written in the MFMA order with its sum.
+            // down product's K, written in the MFMA order with its sum.  Each slot
+            // fragment's 16 rows of 64 bytes go through a stage array of the wave's
+            // own (rows 80 bytes apart, so the 4 lane groups' writes fall in
+            // different banks) and leave as one 16-byte store per lane.
             const int I = ncols, nbh = I >> 5;
             const int hblk = c0 >> 5;
+            constexpr int RB = 80;
+            static_assert(MT * RB <= NT * 48 && NT * 48 <= 2 * MT * 64, "h staging fits");
+            uint8_t* R = wave == 0 ? a0 : wave == 1 ? a1 : wave == 2 ? w0 : w1;
 #pragma unroll
             for (int mf = 0; mf < MF; ++mf) {
                 if (mf < mfa) {
@@ -416,7 +425,7 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                             const float gv = 16.f * acc[mf][f][i], uv = 16.f * acc[mf][2 + f][i];
                             const uint16_t hb = f32_to_bf16(gelu_tanh(gv) * uv);
                             s += bf16_to_f32(hb);
-                            if (ok) h_out[p * I + hblk * 32 + perm_pos(f * 16 + l16)] = hb;
+                            *(uint16_t*)(R + r * RB + 2 * perm_pos(f * 16 + l16)) = hb;
                         }
                         // sum over the 16 lanes holding this row's columns
                         s += dpp_f32<DPP_QUAD_XOR1>(0.f, s);
@@ -425,22 +434,39 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                         s += dpp_f32<DPP_ROW_MIRROR>(0.f, s);
                         if (ok && l16 == 0) hsum_out[p * nbh + hblk] = -1.5f * s;
                     }
+                    const int r = mf * 16 + (lane >> 2), ch = lane & 3;
+                    const uint4 v = *(const uint4*)(R + r * RB + 16 * ch);
+                    if (r < cnt) *(uint4*)(h_out + (int64_t)(base + r) * I + hblk * 32 + 8 * ch) = v;
                 }
             }
         } else {
+            // y through LDS: two slot fragments at a time, a wave turns its 32 slots
+            // x 64 columns (fp32) from the MFMA layout (a lane holds 4 slots of one
+            // column) into rows in a stage array of its own (rows 68 floats apart, so
+            // the 4 lane groups' writes fall in different banks), then writes each
+            // slot's 256 bytes as 16-byte stores (one instruction covers 4 rows
+            // instead of 4 rows x 16 columns of 4-byte stores)
             const int H = ncols;
+            constexpr int RS = 68;
+            static_assert(32 * RS * 4 <= NT * 48 && NT * 48 <= 2 * MT * 64, "y staging fits");
+            float* R = reinterpret_cast<float*>(wave == 0 ? a0 : wave == 1 ? a1 : wave == 2 ? w0 : w1);
+            const int cq = lane & 15;
 #pragma unroll
-            for (int mf = 0; mf < MF; ++mf) {
-                if (mf < mfa) {
+            for (int m2 = 0; m2 < MF; m2 += 2) {
+                if (m2 < mfa) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = mf * 16 + 4 * g + i;
-                        if (r < cnt) {
-                            float* yp = y_out + (int64_t)(base + r) * H + c0 + l16;
+                    for (int h = 0; h < 2; ++h)
 #pragma unroll
-                            for (int nf = 0; nf < 4; ++nf)
-                                if (nf < nfa) yp[nf * 16] = 16.f * acc[mf][nf][i];
-                        }
+                        for (int nf = 0; nf < 4; ++nf)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                R[(16 * h + 4 * g + i) * RS + 16 * nf + l16] = 16.f * acc[m2 + h][nf][i];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const int rl = 4 * q + (lane >> 4), r = 16 * m2 + rl;
+                        const float4 v = *reinterpret_cast<const float4*>(R + rl * RS + 4 * cq);
+                        if (r < cnt && cq < 4 * nfa)
+                            *reinterpret_cast<float4*>(y_out + (int64_t)(base + r) * H + c0 + 4 * cq) = v;
                     }
                 }
             }
