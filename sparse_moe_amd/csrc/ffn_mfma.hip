@@ -353,35 +353,44 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                 }
             }
         };
-        // one iteration: issue pair j + 2 into the stage pair j - 1 used, compute
-        // pair j, wait for this wave's loads of pair j + 1, barrier
+        // One step per pair: issue the loads of a later pair (none past the
+        // last), compute this pair, wait for this wave's loads of the next pair,
+        // barrier.
         if constexpr (LIGHT) {
-            // three stages (the third in arrays of its own): iteration j issues
-            // pair j+2 into the stage pair j-1 used and waits for pair j+1
-            // (issued an iteration earlier)
+            // three stages (the third in arrays of its own): step j issues pair
+            // j+2 into the stage pair j-1 used and waits for pair j+1 (issued a
+            // step earlier)
             const StageRef st2{la2, lc2, w2};
             constexpr int OPS = NA + 4;  // direct loads per wave per pair
             auto step = [&](const StageRef& cur, const StageRef& nxt, int j) {
-                issue(nxt, min(j + 2, npairs - 1));
-                if (active && j < npairs) compute(cur);
-                wait_vmcnt<OPS>();
+                const bool more = j + 2 < npairs;
+                if (more) issue(nxt, j + 2);
+                if (active) compute(cur);
+                if (more)
+                    wait_vmcnt<OPS>();
+                else
+                    wait_vmcnt<0>();
                 stage_barrier();
             };
             issue(st0, 0);
-            issue(st1, min(1, npairs - 1));
-            wait_vmcnt<OPS>();
+            if (npairs > 1) {
+                issue(st1, 1);
+                wait_vmcnt<OPS>();
+            } else {
+                wait_vmcnt<0>();
+            }
             stage_barrier();
             for (int j = 0; j < npairs; j += 3) {
                 step(st0, st2, j);
-                step(st1, st0, j + 1);
-                step(st2, st1, j + 2);
+                if (j + 1 < npairs) step(st1, st0, j + 1);
+                if (j + 2 < npairs) step(st2, st1, j + 2);
             }
         } else {
-            // two stages: iteration j issues pair j+1 into the stage pair j-1
-            // used and waits for it before the barrier
+            // two stages: step j issues pair j+1 into the stage pair j-1 used
+            // and waits for it before the barrier
             auto step = [&](const StageRef& cur, const StageRef& nxt, int j) {
-                issue(nxt, min(j + 1, npairs - 1));
-                if (active && j < npairs) compute(cur);
+                if (j + 1 < npairs) issue(nxt, j + 1);
+                if (active) compute(cur);
                 wait_vmcnt<0>();
                 stage_barrier();
             };
@@ -390,15 +399,11 @@ __global__ __launch_bounds__(256) void ffn_mfma(
             stage_barrier();
             for (int j = 0; j < npairs; j += 2) {
                 step(st0, st1, j);
-                step(st1, st0, j + 1);
+                if (j + 1 < npairs) step(st1, st0, j + 1);
             }
         }
-        // the last (clamped) loads land before the workgroup's LDS is released
-        wait_vmcnt<0>();
-        // the epilogues reuse stage arrays: every wave's loads have landed once
-        // all waves pass this barrier
-        stage_barrier();
-
+        // The last step issues nothing, waits for all of its wave's loads and
+        // ends on the barrier: the stage arrays are free for the epilogues.
         if (!active) return;
         if (MODE == 0) {
             // h = GELU(g) * u for hidden columns c0 .. c0+31: one Q4_0 block of the
