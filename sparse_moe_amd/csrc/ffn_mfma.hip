@@ -174,7 +174,13 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
 // per-lane weight loads that each touched 16 rows.  A third weight stage (two
 // pairs in flight) measured no faster for full tiles; tiles of at most 32
 // slots, which have a quarter of the work per pair, run a three-stage ring.
-template <int MODE>
+//
+// BUF: the activation buffer spans less than 4 GiB.  The direct loads are then
+// buffer loads: a resource per buffer in scalar registers, a fixed 32-bit
+// offset per lane and the pair's offset as a scalar operand, so a load costs no
+// vector address arithmetic (otherwise every load and pair adds a 64-bit
+// address).
+template <int MODE, bool BUF>
 __global__ __launch_bounds__(256) void ffn_mfma(
     const uint16_t* __restrict__ act, const float* __restrict__ csum, const uint8_t* __restrict__ W,
     int nb, int rows_e, int ncols, int n_tiles, const int32_t* __restrict__ offsets,
@@ -236,13 +242,19 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         woff[i] = (uint32_t)row * rowbytes + (pc == 0 ? 0u : pc == 1 ? 16u : 20u);
     }
     // block sums: wave w loads block w >> 1 of tile rows 64 (w & 1) + lane
-    const float* csrc;
+    int64_t cbyte0;  // byte offset in csum
     {
         const int r = 64 * (wave & 1) + lane;
         const int p = base + min(r, cnt - 1);
         const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
-        csrc = csum + arow * nb + (wave >> 1);
+        cbyte0 = (arow * nb + (wave >> 1)) * 4;
     }
+    // buffer resources (unbounded: every offset stays inside its buffer); the
+    // fourth descriptor word selects 32-bit data, as untyped loads need
+    constexpr int RSRC_W3 = 0x00020000;
+    const __amdgpu_buffer_rsrc_t r_act = __builtin_amdgcn_make_buffer_rsrc((void*)act, 0, -1, RSRC_W3);
+    const __amdgpu_buffer_rsrc_t r_cs = __builtin_amdgcn_make_buffer_rsrc((void*)csum, 0, -1, RSRC_W3);
+    const __amdgpu_buffer_rsrc_t r_w = __builtin_amdgcn_make_buffer_rsrc((void*)We, 0, -1, RSRC_W3);
 
     const int mfa = min(8, (cnt + 15) >> 4);  // valid slot fragments
     const bool active = nfa > 0;
@@ -265,7 +277,7 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         // activation loads: the WG's 2 MF instructions t = NA w + i cover block
         // t / MF, rows 16 (t % MF) .. +15; lane: row + (lane >> 2), LDS chunk
         // position lane & 3 holding the row's chunk (lane & 3) ^ ((row >> 2) & 3)
-        const uint16_t* asrc[NA];
+        int64_t abyte[NA];  // byte offsets in act
         int adst[NA];
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
@@ -274,34 +286,52 @@ __global__ __launch_bounds__(256) void ffn_mfma(
             const int p = base + min(r, cnt - 1);
             const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
             const int chunk = (lane & 3) ^ ((r >> 2) & 3);
-            asrc[i] = act + arow * nb * 32 + blk * 32 + 8 * chunk;
+            abyte[i] = (arow * nb * 32 + blk * 32 + 8 * chunk) * 2;
             adst[i] = blk * AROWS * 64 + rg * 1024;
         }
         // block sums: a heavy stage takes block w >> 1 of rows 64 (w & 1) + lane
         // from wave w; a light stage its 2 x 32 sums (block lane >> 5, row
         // lane & 31) from every wave alike (the same bytes, so the four copies
         // agree)
-        const float* cs = csrc;
+        int64_t cbyte = cbyte0;
         int cdst = 64 * wave;
         if constexpr (LIGHT) {
             const int r = lane & 31;
             const int p = base + min(r, cnt - 1);
             const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
-            cs = csum + arow * nb + (lane >> 5);
+            cbyte = (arow * nb + (lane >> 5)) * 4;
             cdst = 0;
         }
+        // pair j: activations 128 bytes, block sums 8 bytes and weights 36 bytes
+        // further on
         auto issue = [&](const StageRef& S, int j) {
+            if constexpr (BUF) {
 #pragma unroll
-            for (int i = 0; i < NA; ++i)
-                __builtin_amdgcn_global_load_lds((glb_void_t*)(asrc[i] + 64 * j),
-                                                 (lds_void_t*)(S.a + adst[i]), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((glb_void_t*)(cs + 2 * j),
-                                             (lds_void_t*)(S.c + cdst), 4, 0, 0);
+                for (int i = 0; i < NA; ++i)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(r_act, (lds_void_t*)(S.a + adst[i]), 16,
+                                                             (int)abyte[i], 128 * j, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r_cs, (lds_void_t*)(S.c + cdst), 4,
+                                                         (int)cbyte, 8 * j, 0, 0);
 #pragma unroll
-            for (int i = 0; i < 3; ++i)
-                __builtin_amdgcn_global_load_lds((glb_void_t*)(We + woff[i] + 36u * (uint32_t)j),
-                                                 (lds_void_t*)(S.w + 64 * 48 * wave + 1024 * i), 16,
-                                                 0, 0);
+                for (int i = 0; i < 3; ++i)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        r_w, (lds_void_t*)(S.w + 64 * 48 * wave + 1024 * i), 16, (int)woff[i], 36 * j,
+                        0, 0);
+            } else {
+                const uint8_t* act_b = reinterpret_cast<const uint8_t*>(act);
+                const uint8_t* cs_b = reinterpret_cast<const uint8_t*>(csum);
+#pragma unroll
+                for (int i = 0; i < NA; ++i)
+                    __builtin_amdgcn_global_load_lds((glb_void_t*)(act_b + abyte[i] + 128 * j),
+                                                     (lds_void_t*)(S.a + adst[i]), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((glb_void_t*)(cs_b + cbyte + 8 * j),
+                                                 (lds_void_t*)(S.c + cdst), 4, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+                    __builtin_amdgcn_global_load_lds(
+                        (glb_void_t*)(We + woff[i] + 36u * (uint32_t)j),
+                        (lds_void_t*)(S.w + 64 * 48 * wave + 1024 * i), 16, 0, 0);
+            }
         };
         const int swz = 16 * (g ^ ((l16 >> 2) & 3));  // this lane's chunk position in a row
         const int q1off = g < 3 ? 20 + 4 * g : 44;     // qs1 dword g in a row's 48 bytes
@@ -541,6 +571,11 @@ size_t ffn_mfma_ws_bytes(int64_t T, int H, int I, int64_t N) {
            align256((size_t)N * I * 2) + align256((size_t)N * (I / 32) * 4);
 }
 
+// Buffer loads take 32-bit offsets: every byte of an activation buffer of this
+// size (its block sums are a sixteenth of it, one expert's weights at most
+// 2 x MOE_MAX_I rows of MOE_MAX_H / 32 blocks) is reachable.
+static bool buf_ok(size_t act_bytes) { return act_bytes < ((size_t)1 << 31); }
+
 hipError_t launch_ffn_mfma(const void* x, int64_t T, int H, const uint8_t* w_gate_up,
                            const uint8_t* w_down, int I, int E, int K, int N,
                            const int32_t* offsets, const int32_t* sorted_slots, void* ws,
@@ -563,14 +598,22 @@ hipError_t launch_ffn_mfma(const void* x, int64_t T, int H, const uint8_t* w_gat
     {
         const int n_tiles = (I + NT / 2 - 1) / (NT / 2);
         const int total = (mtiles * n_tiles + 7) / 8 * 8;
-        ffn_mfma<0><<<total, 256, 0, st>>>(xp, xs, w_gate_up, H / 32, 2 * I, I, n_tiles,
-                                                   offsets, sorted_slots, K, E, hp, hs, nullptr);
+        if (buf_ok((size_t)T * H * 2))
+            ffn_mfma<0, true><<<total, 256, 0, st>>>(xp, xs, w_gate_up, H / 32, 2 * I, I, n_tiles,
+                                                     offsets, sorted_slots, K, E, hp, hs, nullptr);
+        else
+            ffn_mfma<0, false><<<total, 256, 0, st>>>(xp, xs, w_gate_up, H / 32, 2 * I, I, n_tiles,
+                                                      offsets, sorted_slots, K, E, hp, hs, nullptr);
     }
     {
         const int n_tiles = (H + NT - 1) / NT;
         const int total = (mtiles * n_tiles + 7) / 8 * 8;
-        ffn_mfma<1><<<total, 256, 0, st>>>(hp, hs, w_down, I / 32, H, H, n_tiles, offsets,
-                                                   sorted_slots, K, E, nullptr, nullptr, y_sorted);
+        if (buf_ok((size_t)N * I * 2))
+            ffn_mfma<1, true><<<total, 256, 0, st>>>(hp, hs, w_down, I / 32, H, H, n_tiles, offsets,
+                                                     sorted_slots, K, E, nullptr, nullptr, y_sorted);
+        else
+            ffn_mfma<1, false><<<total, 256, 0, st>>>(hp, hs, w_down, I / 32, H, H, n_tiles, offsets,
+                                                      sorted_slots, K, E, nullptr, nullptr, y_sorted);
     }
     return hipGetLastError();
 }
@@ -589,8 +632,12 @@ hipError_t launch_linear_mfma(const void* x, int64_t T, int H, const uint8_t* W,
     const int N = (int)T, mtiles = N / MT + 1;
     const int n_tiles = (R + NT - 1) / NT;
     const int total = (mtiles * n_tiles + 7) / 8 * 8;
-    ffn_mfma<1><<<total, 256, 0, st>>>(xp, xs, W, H / 32, R, R, n_tiles, offsets, slots, 1,
-                                               1, nullptr, nullptr, y);
+    if (buf_ok((size_t)T * H * 2))
+        ffn_mfma<1, true><<<total, 256, 0, st>>>(xp, xs, W, H / 32, R, R, n_tiles, offsets, slots, 1,
+                                                 1, nullptr, nullptr, y);
+    else
+        ffn_mfma<1, false><<<total, 256, 0, st>>>(xp, xs, W, H / 32, R, R, n_tiles, offsets, slots,
+                                                  1, 1, nullptr, nullptr, y);
     return hipGetLastError();
 }
 
