@@ -154,10 +154,10 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
 // tile (4 MFMA row fragments) against all MT slots (8 fragments), 128 fp32
 // accumulators per lane.
 //
-// Every operand goes through LDS by direct loads (global_load_lds), two stages
-// in turn: iteration j issues the loads of pair j+1 into the stage pair j-1
-// used, runs the MFMAs of pair j, waits for its own loads and ends on a
-// barrier, so no register holds staged data.  A stage is the activations
+// Every operand goes through LDS by direct loads (buffer loads with the lds
+// modifier), two stages in turn: iteration j issues the loads of pair j+1 into
+// the stage pair j-1 used, runs the MFMAs of pair j, waits for its own loads
+// and ends on a barrier, so no register holds staged data.  A stage is the activations
 // [2 blocks][MT rows][64 B] (the 16-byte chunks of a row rotated by
 // (row >> 2) & 3, so the fragment reads are conflict-free), their block sums
 // [2][MT] and the tile's weight rows [NT][48 B] (a row's 36 bytes of the pair
