@@ -157,9 +157,9 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
 // Every operand goes through LDS by direct loads (buffer loads with the lds
 // modifier), two stages in turn: iteration j issues the loads of pair j+1 into
 // the stage pair j-1 used, runs the MFMAs of pair j, waits for its own loads
-// and ends on a barrier, so no register holds staged data.  A stage is the activations
-// [2 blocks][MT rows][64 B] (the 16-byte chunks of a row rotated by
-// (row >> 2) & 3, so the fragment reads are conflict-free), their block sums
+// and ends on a barrier, so no register holds staged data.  A stage is the
+// activations [2 blocks][MT rows][64 B] (the 16-byte chunks of a row rotated
+// by (row >> 2) & 3, so the fragment reads are conflict-free), their block sums
 // [2][MT] and the tile's weight rows [NT][48 B] (a row's 36 bytes of the pair
 // as its bytes 0-15, 16-31 and 20-35: direct loads of 12 bytes would land 16
 // bytes apart, so three 16-byte loads that never cross the pair).  Each part
@@ -175,11 +175,12 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
 // pairs in flight) measured no faster for full tiles; tiles of at most 32
 // slots, which have a quarter of the work per pair, run a three-stage ring.
 //
-// BUF: the activation buffer spans less than 4 GiB.  The direct loads are then
-// buffer loads: a resource per buffer in scalar registers, a fixed 32-bit
-// offset per lane and the pair's offset as a scalar operand, so a load costs no
-// vector address arithmetic (otherwise every load and pair adds a 64-bit
-// address).
+// BUF: the activation buffer spans less than 2 GiB (its block sums and one
+// expert's weights are smaller still), so every offset fits a signed 32-bit
+// lane offset.  The direct loads are then buffer loads: a resource per buffer
+// in scalar registers, a fixed offset per lane and the pair's offset as a
+// scalar operand, so a load costs no vector address arithmetic (otherwise
+// every load and pair adds a 64-bit address).
 template <int MODE, bool BUF>
 __global__ __launch_bounds__(256) void ffn_mfma(
     const uint16_t* __restrict__ act, const float* __restrict__ csum, const uint8_t* __restrict__ W,
