@@ -103,18 +103,22 @@ MOE_DEV void digitize_quarter(const float v[8], int m, uint32_t* words, int wstr
 }
 
 // signed 4-bit codes (q - 8) of one Q4_0 block times the 4 digit words of each
-// qs dword: exact integer sum_j (q_j - 8) n_j
+// qs dword: exact integer sum_j (q_j - 8) n_j.  The digit sums are combined by
+// Horner's rule, each digit's dot products accumulating onto 16 times the sum
+// so far (|sum| < 2^24, exact in int32): one shift per digit instead of a
+// zeroed accumulator per digit and a final shift-and-add.
 MOE_DEV int block_idot(const uint32_t q[4], const uint32_t* x16) {
-    int d0 = 0, d1 = 0, d2 = 0, d3 = 0;
+    int qm[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int qm = (int)(q[m] ^ 0x88888888u);
-        d0 = __builtin_amdgcn_sdot8(qm, (int)x16[4 * m + 0], d0, false);
-        d1 = __builtin_amdgcn_sdot8(qm, (int)x16[4 * m + 1], d1, false);
-        d2 = __builtin_amdgcn_sdot8(qm, (int)x16[4 * m + 2], d2, false);
-        d3 = __builtin_amdgcn_sdot8(qm, (int)x16[4 * m + 3], d3, false);
+    for (int m = 0; m < 4; ++m) qm[m] = (int)(q[m] ^ 0x88888888u);
+    int d = 0;
+#pragma unroll
+    for (int k = 3; k >= 0; --k) {
+        d <<= 4;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) d = __builtin_amdgcn_sdot8(qm[m], (int)x16[4 * m + k], d, false);
     }
-    return d0 + (d1 << 4) + (d2 << 8) + (d3 << 12);
+    return d;
 }
 
 // Scales and qs dwords of a block pair: block A at bytes 0..17, block B at
