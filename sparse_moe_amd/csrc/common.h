@@ -89,17 +89,28 @@ constexpr int DPP_ROW_MIRROR = 0x140;
 constexpr int DPP_ROW_BCAST15 = 0x142;
 constexpr int DPP_ROW_BCAST31 = 0x143;
 
+// DPP move without an `old` operand (lanes without a source lane read 0), so
+// no register has to be prepared for the lanes it does not write.
+template <int CTRL>
+MOE_DEV float dpp_mov_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
 // Sum over aligned groups of G lanes (G a power of two <= 64).  The result is
-// valid in lane G-1 of each group (and in every lane of the group for G <= 16).
-// Every lane of the wave must be active.
+// valid in lane G-1 of each group (and in every lane of the group for G <= 16;
+// for G >= 32 the other lanes hold partial sums).  Every lane of the wave must
+// be active.
 template <int G>
 MOE_DEV float group_sum(float v) {
-    if (G >= 2) v += dpp_f32<DPP_QUAD_XOR1>(v, v);
-    if (G >= 4) v += dpp_f32<DPP_QUAD_XOR2>(v, v);
-    if (G >= 8) v += dpp_f32<DPP_ROW_HALF_MIRROR>(v, v);
-    if (G >= 16) v += dpp_f32<DPP_ROW_MIRROR>(v, v);
-    if (G >= 32) v += dpp_f32<DPP_ROW_BCAST15, 0xA>(0.f, v);
-    if (G >= 64) v += dpp_f32<DPP_ROW_BCAST31, 0xC>(0.f, v);
+    if (G >= 2) v += dpp_mov_f32<DPP_QUAD_XOR1>(v);
+    if (G >= 4) v += dpp_mov_f32<DPP_QUAD_XOR2>(v);
+    if (G >= 8) v += dpp_mov_f32<DPP_ROW_HALF_MIRROR>(v);
+    if (G >= 16) v += dpp_mov_f32<DPP_ROW_MIRROR>(v);
+    // lane 15 of each row onto the next row: rows 1 and 3 then hold the sums
+    // of lanes 0-31 and 32-63 (rows 0 and 2 are not used)
+    if (G >= 32) v += dpp_mov_f32<DPP_ROW_BCAST15>(v);
+    // lane 31 onto rows 2 and 3: lane 63 holds the sum of all 64 lanes
+    if (G >= 64) v += dpp_mov_f32<DPP_ROW_BCAST31>(v);
     return v;
 }
 
