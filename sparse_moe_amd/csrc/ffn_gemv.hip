@@ -58,8 +58,8 @@ MOE_DEV void digitize_quarter(const float v[8], int m, uint32_t* words, int wstr
     float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    amax = fmaxf(amax, dpp_f32<DPP_QUAD_XOR1>(amax, amax));
-    amax = fmaxf(amax, dpp_f32<DPP_QUAD_XOR2>(amax, amax));
+    amax = fmaxf(amax, dpp_mov_f32<DPP_QUAD_XOR1>(amax));
+    amax = fmaxf(amax, dpp_mov_f32<DPP_QUAD_XOR2>(amax));
     uint32_t wd[4] = {0u, 0u, 0u, 0u};
     float s = 0.f;
     if (amax > 0.f) {

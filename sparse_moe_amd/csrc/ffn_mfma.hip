@@ -464,10 +464,10 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                             *(uint16_t*)(R + r * RB + 2 * perm_pos(f * 16 + l16)) = hb;
                         }
                         // sum over the 16 lanes holding this row's columns
-                        s += dpp_f32<DPP_QUAD_XOR1>(0.f, s);
-                        s += dpp_f32<DPP_QUAD_XOR2>(0.f, s);
-                        s += dpp_f32<DPP_ROW_HALF_MIRROR>(0.f, s);
-                        s += dpp_f32<DPP_ROW_MIRROR>(0.f, s);
+                        s += dpp_mov_f32<DPP_QUAD_XOR1>(s);
+                        s += dpp_mov_f32<DPP_QUAD_XOR2>(s);
+                        s += dpp_mov_f32<DPP_ROW_HALF_MIRROR>(s);
+                        s += dpp_mov_f32<DPP_ROW_MIRROR>(s);
                         if (ok && l16 == 0) hsum_out[p * nbh + hblk] = -1.5f * s;
                     }
                     const int r = mf * 16 + (lane >> 2), ch = lane & 3;
@@ -538,8 +538,8 @@ __global__ __launch_bounds__(256) void ffn_mfma_prep(const uint16_t* __restrict_
         s += __uint_as_float(w4[i] << 16);
         s += __uint_as_float(w4[i] & 0xFFFF0000u);
     }
-    s += dpp_f32<DPP_QUAD_XOR1>(s, s);
-    s += dpp_f32<DPP_QUAD_XOR2>(s, s);
+    s += dpp_mov_f32<DPP_QUAD_XOR1>(s);
+    s += dpp_mov_f32<DPP_QUAD_XOR2>(s);
     constexpr int FROM_LO = 0x50;  // quad_perm [0,0,1,1]: lane c reads lane c >> 1
     constexpr int FROM_HI = 0xFA;  // quad_perm [2,2,3,3]: lane c reads lane (c >> 1) + 2
     auto mv = [](uint32_t a, auto ctrl) {

@@ -180,28 +180,35 @@ MOE_DEV int topk_key(float v) {
 }
 MOE_DEV float topk_unkey(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
 
-template <int CTRL, int ROW_MASK = 0xF>
-MOE_DEV int dpp_i32(int old, int v) {
-    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
+// DPP move without an `old` operand (lanes without a source lane read 0): the
+// compiler folds it into the min or max that consumes it.
+template <int CTRL>
+MOE_DEV int dpp_mov_i32(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 
+// Wave-wide minimum and maximum, read from lane 63.  The two row broadcasts
+// write every row: rows 1 and 3 take lane 15 of the row before (row 0's lanes
+// read 0 and row 2's mix rows 1 and 2; neither reaches lane 63), then rows 2
+// and 3 take lane 31, which holds the extremum of rows 0 and 1.
+
 MOE_DEV int wave_min_i32(int v) {
-    v = min(v, dpp_i32<DPP_QUAD_XOR1>(v, v));
-    v = min(v, dpp_i32<DPP_QUAD_XOR2>(v, v));
-    v = min(v, dpp_i32<DPP_ROW_HALF_MIRROR>(v, v));
-    v = min(v, dpp_i32<DPP_ROW_MIRROR>(v, v));
-    v = min(v, dpp_i32<DPP_ROW_BCAST15, 0xA>(INT_MAX, v));
-    v = min(v, dpp_i32<DPP_ROW_BCAST31, 0xC>(INT_MAX, v));
+    v = min(v, dpp_mov_i32<DPP_QUAD_XOR1>(v));
+    v = min(v, dpp_mov_i32<DPP_QUAD_XOR2>(v));
+    v = min(v, dpp_mov_i32<DPP_ROW_HALF_MIRROR>(v));
+    v = min(v, dpp_mov_i32<DPP_ROW_MIRROR>(v));
+    v = min(v, dpp_mov_i32<DPP_ROW_BCAST15>(v));
+    v = min(v, dpp_mov_i32<DPP_ROW_BCAST31>(v));
     return __builtin_amdgcn_readlane(v, 63);
 }
 
 MOE_DEV int wave_max_i32(int v) {
-    v = max(v, dpp_i32<DPP_QUAD_XOR1>(v, v));
-    v = max(v, dpp_i32<DPP_QUAD_XOR2>(v, v));
-    v = max(v, dpp_i32<DPP_ROW_HALF_MIRROR>(v, v));
-    v = max(v, dpp_i32<DPP_ROW_MIRROR>(v, v));
-    v = max(v, dpp_i32<DPP_ROW_BCAST15, 0xA>(INT_MIN, v));
-    v = max(v, dpp_i32<DPP_ROW_BCAST31, 0xC>(INT_MIN, v));
+    v = max(v, dpp_mov_i32<DPP_QUAD_XOR1>(v));
+    v = max(v, dpp_mov_i32<DPP_QUAD_XOR2>(v));
+    v = max(v, dpp_mov_i32<DPP_ROW_HALF_MIRROR>(v));
+    v = max(v, dpp_mov_i32<DPP_ROW_MIRROR>(v));
+    v = max(v, dpp_mov_i32<DPP_ROW_BCAST15>(v));
+    v = max(v, dpp_mov_i32<DPP_ROW_BCAST31>(v));
     return __builtin_amdgcn_readlane(v, 63);
 }
 
