@@ -157,8 +157,18 @@ moe_status moe_route(const void* x, int x_dt, int64_t T, int32_t H, const float*
  *              (holds the hidden h); contents need no initialisation
  * Per slot: g = Wg x, u = Wu x, h = GELU_tanh(g) * u rounded to x_dt (the
  * hidden is materialised in the activation type), y = Wd h; GELU_tanh(z) =
- * z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).  Accumulation is fp32 or exact
- * integer; dequantised weights are never rounded.
+ * z/2 (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).  Dequantised weights are never
+ * rounded; accumulation is fp32.  The two paths treat the activations
+ * differently:
+ *  - GEMV path (fewer than 64 tokens, or fp32 activations, or H or I not a
+ *    multiple of 64): each 32-element block of the activations (x for
+ *    gate/up, h for down) is first rounded to 15-bit fixed point relative to
+ *    the block's largest magnitude m, n = rint(v * 30583 / m), an error of at
+ *    most m / 61166 per element; the block's products with the 4-bit codes
+ *    are then exact integers, scaled by d * m / 30583 in fp32.
+ *  - MFMA path (bf16 activations, at least 64 tokens, H and I multiples of
+ *    64): the bf16 activations enter bf16 MFMAs exactly (exact products, fp32
+ *    accumulation per Q4_0 block, then times d).
  */
 size_t moe_expert_ffn_q4_0_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_t I,
                                            int32_t E, int x_dt);
@@ -180,9 +190,11 @@ moe_status moe_expert_ffn_q4_0(const void* x, int x_dt, int64_t T, int32_t H,
  *   ws  >= moe_linear_q4_0_workspace_bytes(T, H, R, x_dt) bytes, 16-byte
  *       aligned; contents need no initialisation
  * The same kernels as the experts' down product (one expert holding every
- * token): Q4_0 GEMV with exact integer block products for few tokens, exact
- * bf16 MFMA products for bf16 activations from 64 tokens (H % 64 == 0 and
- * R % 16 == 0); fp32 accumulation, weights never rounded.
+ * token): for few tokens the Q4_0 GEMV, which rounds each 32-element block of x
+ * to 15-bit fixed point relative to its largest magnitude m (error <= m / 61166
+ * per element) and then takes exact integer block products; for bf16
+ * activations from 64 tokens (H % 64 == 0 and R % 16 == 0) exact bf16 MFMA
+ * products.  fp32 accumulation, weights never rounded.
  */
 size_t moe_linear_q4_0_workspace_bytes(int64_t T, int32_t H, int32_t R, int x_dt);
 moe_status moe_linear_q4_0(const void* x, int x_dt, int64_t T, int32_t H, const void* W,

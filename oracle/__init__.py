@@ -61,7 +61,10 @@ def lib() -> C.CDLL:
         L.orc_rmsnorm.argtypes = [p, i32, p, d, i64, i32, p]
         L.orc_moe_layer.argtypes = [p, i32, i64, i32, p, p, p, p, i32, i32, p, p, i32, p, p,
                                     p, p, p, p, p, p, p]
-        for f in ("orc_router_logits", "orc_topk_softmax", "orc_topk_weights", "orc_permute", "orc_expert_ffn_token",
+        L.orc_residual.argtypes = [p, p, i64, i32, p, p]
+        L.orc_stack_layer.argtypes = [p, i64, i32, p, d, p, p, i32, i32, p, p, i32, p, p, p, p, p,
+                                      p]
+        for f in ("orc_residual", "orc_stack_layer", "orc_router_logits", "orc_topk_softmax", "orc_topk_weights", "orc_permute", "orc_expert_ffn_token",
                   "orc_expert_ffn", "orc_linear_q4_0", "orc_combine", "orc_rmsnorm", "orc_moe_layer"):
             getattr(L, f).restype = i32
         _lib = L
@@ -246,3 +249,37 @@ def moe_layer(x, w_r, w_gate_up, w_down, K: int, scale=None, bias=None, r_scale=
                                _ptr(logits), _ptr(ids), _ptr(w), _ptr(off), _ptr(ss), _ptr(sp),
                                _ptr(out)), "orc_moe_layer")
     return dict(logits=logits, ids=ids, w=w, offsets=off, sorted_slots=ss, slot_pos=sp, out=out)
+
+
+def residual(x_bf16, out, token_mask=None) -> np.ndarray:
+    """x_next = bf16(x + out) (bf16 bits as uint16; out binary64)."""
+    x = np.ascontiguousarray(x_bf16, np.uint16)
+    T, H = x.shape
+    o = np.ascontiguousarray(out, np.float64)
+    assert o.shape == (T, H)
+    m = None if token_mask is None else np.ascontiguousarray(token_mask, np.uint8)
+    xn = np.zeros((T, H), np.uint16)
+    _check(lib().orc_residual(_ptr(x), _ptr(o), T, H, _ptr(m), _ptr(xn)), "orc_residual")
+    return xn
+
+
+def stack_layer(x_bf16, rms_w, eps: float, w_r, w_gate_up, w_down, K: int, scale=None,
+                bias=None, token_mask=None) -> dict:
+    """One pre-norm block of the stack; returns dict(xhat, ids, out, x_next)."""
+    x = np.ascontiguousarray(x_bf16, np.uint16)
+    T, H = x.shape
+    E = w_gate_up.shape[0]
+    I = w_gate_up.shape[1] // 2
+    xhat = np.zeros((T, H), np.uint16)
+    ids = np.zeros((T, K), np.int32)
+    out = np.zeros((T, H), np.float64)
+    xn = np.zeros((T, H), np.uint16)
+    sc = None if scale is None else np.ascontiguousarray(scale, np.float32)
+    bs = None if bias is None else np.ascontiguousarray(bias, np.float32)
+    m = None if token_mask is None else np.ascontiguousarray(token_mask, np.uint8)
+    _check(lib().orc_stack_layer(_ptr(x), T, H, _ptr(np.ascontiguousarray(rms_w, np.float32)),
+                                 eps, _ptr(np.ascontiguousarray(w_r, np.float32)), _ptr(bs), E, K,
+                                 _ptr(np.ascontiguousarray(w_gate_up)),
+                                 _ptr(np.ascontiguousarray(w_down)), I, _ptr(sc), _ptr(m),
+                                 _ptr(xhat), _ptr(ids), _ptr(out), _ptr(xn)), "orc_stack_layer")
+    return dict(xhat=xhat, ids=ids, out=out, x_next=xn)

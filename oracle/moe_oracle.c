@@ -331,3 +331,50 @@ int orc_moe_layer(const void* x, int x_dt, int64_t T, int H, const float* w_r,
     if (!logits) free(l);
     return rc;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Stack: residual add and one pre-norm block                                */
+
+/* The stack's residual stream is bf16 (the stack workload's activations);
+ * the layer output is added to it and the sum rounded once to bf16. */
+int orc_residual(const uint16_t* x_bf16, const double* out, int64_t T, int H,
+                 const uint8_t* token_mask, uint16_t* x_next) {
+    if (T < 0 || H <= 0 || !x_bf16 || !out || !x_next) return 1;
+    for (int64_t t = 0; t < T; ++t) {
+        if (token_mask && !token_mask[t]) continue;
+        for (int j = 0; j < H; ++j) {
+            size_t i = (size_t)t * (size_t)H + (size_t)j;
+            x_next[i] = orc_f64_to_bf16(orc_bf16_to_f64(x_bf16[i]) + out[i]);
+        }
+    }
+    return 0;
+}
+
+/* Model card, table "What is inside": the norms are FP32 (here binary64 in the
+ * oracle); the norm precedes the routed layer and the residual follows it. */
+int orc_stack_layer(const uint16_t* x_bf16, int64_t T, int H, const float* rms_w, double eps,
+                    const float* w_r, const float* bias, int E, int K, const uint8_t* w_gate_up,
+                    const uint8_t* w_down, int I, const float* scale, const uint8_t* token_mask,
+                    uint16_t* xhat_out, int32_t* ids_out, double* out_out, uint16_t* x_next) {
+    if (T < 0 || H <= 0 || K <= 0 || K > E || !x_bf16 || !rms_w || !w_r || !x_next) return 1;
+    size_t n = (size_t)T * (size_t)H;
+    uint16_t* xhat = (uint16_t*)malloc(sizeof(uint16_t) * (n + 1));
+    double* out = (double*)malloc(sizeof(double) * (n + 1));
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * ((size_t)T * K + 1));
+    double* w = (double*)malloc(sizeof(double) * ((size_t)T * K + 1));
+    int32_t* off = (int32_t*)malloc(sizeof(int32_t) * ((size_t)E + 1));
+    int32_t* ss = (int32_t*)malloc(sizeof(int32_t) * ((size_t)T * K + 1));
+    int32_t* sp = (int32_t*)malloc(sizeof(int32_t) * ((size_t)T * K + 1));
+    int rc = (!xhat || !out || !ids || !w || !off || !ss || !sp) ? 2 : 0;
+    for (size_t i = 0; !rc && i < n; ++i) out[i] = NAN;  /* rows of unselected tokens */
+    if (!rc) rc = orc_rmsnorm(x_bf16, ORC_BF16, rms_w, eps, T, H, xhat);
+    if (!rc)
+        rc = orc_moe_layer(xhat, ORC_BF16, T, H, w_r, NULL, NULL, bias, E, K, w_gate_up, w_down, I,
+                           scale, token_mask, NULL, ids, w, off, ss, sp, out);
+    if (!rc) rc = orc_residual(x_bf16, out, T, H, token_mask, x_next);
+    if (!rc && xhat_out) memcpy(xhat_out, xhat, sizeof(uint16_t) * n);
+    if (!rc && ids_out) memcpy(ids_out, ids, sizeof(int32_t) * (size_t)T * K);
+    if (!rc && out_out) memcpy(out_out, out, sizeof(double) * n);
+    free(xhat); free(out); free(ids); free(w); free(off); free(ss); free(sp);
+    return rc;
+}

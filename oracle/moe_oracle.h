@@ -110,6 +110,24 @@ int orc_moe_layer(const void* x, int x_dt, int64_t T, int H, const float* w_r,
                   const uint8_t* token_mask, double* logits, int32_t* ids, double* w,
                   int32_t* offsets, int32_t* sorted_slots, int32_t* slot_pos, double* out);
 
+/* Residual add between the blocks of the stack: x_next = bf16(x + out), with
+ * x the bf16 residual stream and out the layer's combined output (binary64),
+ * added exactly and rounded once, to nearest even.  token_mask nullable (rows
+ * of unselected tokens untouched). */
+int orc_residual(const uint16_t* x_bf16, const double* out, int64_t T, int H,
+                 const uint8_t* token_mask, uint16_t* x_next);
+
+/* One block of the stack, pre-norm: xhat = RMSNorm(x) (bf16), the routed
+ * layer on xhat (router with the additive prior `bias`, experts and the
+ * combine as in orc_moe_layer), then x_next = bf16(x + out).  token_mask as in
+ * orc_moe_layer (routing covers every token; the FFN, the combine and the
+ * residual only the selected ones).  xhat_out, ids, out: nullable [T,H] bf16,
+ * [T,K] int32, [T,H] binary64 copies of the intermediate results. */
+int orc_stack_layer(const uint16_t* x_bf16, int64_t T, int H, const float* rms_w, double eps,
+                    const float* w_r, const float* bias, int E, int K, const uint8_t* w_gate_up,
+                    const uint8_t* w_down, int I, const float* scale, const uint8_t* token_mask,
+                    uint16_t* xhat_out, int32_t* ids_out, double* out_out, uint16_t* x_next);
+
 #ifdef __cplusplus
 }
 #endif

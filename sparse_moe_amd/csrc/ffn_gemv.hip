@@ -14,7 +14,11 @@
 // four balanced base-16 digits (each in [-8, 7]); the block's integer dot
 // sum_j (q_j - 8) n_j is therefore exact, and the block contributes
 // d * (max|v| / 30583) * dot.  The only approximation is the 15-bit fixed
-// point of the activations (|error| <= max|v| / 61166 per element).
+// point of the activations (|error| <= max|v| / 61166 per element, max|v| the
+// largest magnitude of the element's 32-element block); it applies to fp32 and
+// bf16 activations alike, and to the hidden h of the down product.  A block
+// whose largest magnitude is below the fp32 normal range keeps that bound only
+// as far as its scale max|v| / 30583 is representable.
 //
 // Lane layout: a lane owns a pair of consecutive blocks (36 bytes, always
 // 4-byte aligned) at the same position of every row it visits, so the lane's
@@ -63,12 +67,15 @@ MOE_DEV void digitize_quarter(const float v[8], int m, uint32_t* words, int wstr
     uint32_t wd[4] = {0u, 0u, 0u, 0u};
     float s = 0.f;
     if (amax > 0.f) {
-        const float inv = (float)DIGIT_NMAX / amax;
+        // blocks below 2^-64 are scaled up by 2^64 (exactly) first, so that
+        // DIGIT_NMAX / amax stays finite down to the smallest subnormal
+        const float pre = amax < 0x1p-64f ? 0x1p64f : 1.f;
+        const float inv = (float)DIGIT_NMAX / (amax * pre);
         s = amax / (float)DIGIT_NMAX;
         uint32_t u[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            int n = (int)rintf(v[j] * inv);
+            int n = (int)rintf((v[j] * pre) * inv);
             n = max(-DIGIT_NMAX, min(DIGIT_NMAX, n));
             // n + 0x8888 = sum_k h_k 16^k with hex digits h_k, so n = sum_k (h_k - 8) 16^k:
             // the balanced digits are h_k - 8, whose 4-bit two's complement is h_k ^ 8

@@ -87,11 +87,13 @@ def check_routing(L, g: dict, logits_ref: np.ndarray):
     return ids_eff, w_ref, int(ties.sum())
 
 
-def check_layer(L, g: dict, logits_in=None, token_sample=None, check_y_full=True):
+def check_layer(L, g: dict, logits_in=None, token_sample=None, refs=None):
     """Full comparison of one layer's GPU outputs against the oracle.
 
     token_sample: indices of tokens whose expert outputs and combined output the
-    oracle computes (None: all tokens)."""
+    oracle computes (None: all tokens).  refs: a dict that receives the oracle's
+    combined output ("out", binary64, rows of unsampled tokens NaN) and the
+    effective expert ids ("ids")."""
     K, E = L.spec.K, L.spec.E
     if logits_in is None:
         logits_ref = oracle.router_logits(L.x, L.w_router, bias=L.router_bias)
@@ -120,4 +122,7 @@ def check_layer(L, g: dict, logits_in=None, token_sample=None, check_y_full=True
     oe = max_rel(g["out"][sel], out_ref[sel])
     assert oe <= TOL, "combined output rel err %g" % oe
     assert np.all(np.isfinite(g["out"])), "non-finite output"
+    if refs is not None:
+        refs["out"] = out_ref
+        refs["ids"] = ids_eff
     return dict(y_err=ye, out_err=oe, near_ties=nties, distinct_experts=int((np.diff(off) > 0).sum()))

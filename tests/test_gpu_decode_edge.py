@@ -1,0 +1,123 @@
+"""Edge cases of the decode path's own approximation, at the Gemma shape.
+
+The decode GEMV rounds each 32-element activation block (x for gate/up, h for
+down) to 15-bit fixed point relative to the block's largest magnitude before
+its exact integer products.  These cases aim at the weak spots of that
+rounding and of the Q4_0 scale handling:
+
+  * a block with one outlier 10^3..10^4 times its neighbours,
+  * blocks of tiny magnitude (1e-30) and fp32-subnormal blocks (1e-40),
+  * all-zero blocks and an all-zero token,
+  * Q4_0 blocks with negative scales d (real ggml blocks have them).
+
+Each token is compared with the oracle on its own scale: per slot,
+max|y_gpu - y_ref| <= 2e-3 * max|y_ref|, and per token the same for the combined
+output (exact zeros where the reference is zero); ids bit-exact under the
+near-tie rule.  1-token decode with fp32 activations and 8-token decode with
+bf16 activations, fused and separate routing."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+from sparse_moe_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+CASES = ("outlier_1e3_every_block", "outlier_1e4_some_blocks", "tiny_blocks_1e-30",
+         "tiny_token_1e-30", "zero_blocks", "subnormal_blocks_1e-40", "zero_token", "plain")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def shape_token(v: np.ndarray, case: str, g: np.random.Generator) -> np.ndarray:
+    """One fp32 activation row [H] reshaped into the named case."""
+    v = v.astype(np.float32).copy()
+    blk = v.reshape(-1, 32)
+    nb = blk.shape[0]
+    if case == "outlier_1e3_every_block":
+        j = g.integers(0, 32, size=nb)
+        blk[np.arange(nb), j] *= np.float32(1e3)
+    elif case == "outlier_1e4_some_blocks":
+        b = g.choice(nb, nb // 4, replace=False)
+        blk[b, g.integers(0, 32, size=b.size)] = np.float32(1e4) * np.sign(g.standard_normal(b.size))
+    elif case == "tiny_blocks_1e-30":
+        b = g.choice(nb, nb // 3, replace=False)
+        blk[b] *= np.float32(1e-30)
+    elif case == "tiny_token_1e-30":
+        blk *= np.float32(1e-30)
+    elif case == "zero_blocks":
+        blk[g.choice(nb, nb // 3, replace=False)] = 0
+    elif case == "subnormal_blocks_1e-40":
+        b = g.choice(nb, nb // 3, replace=False)
+        blk[b] = (blk[b] * np.float32(1e-40)).astype(np.float32)
+    elif case == "zero_token":
+        blk[:] = 0
+    return blk.reshape(-1)
+
+
+def negate_some_scales(q: np.ndarray, g: np.random.Generator) -> np.ndarray:
+    """Flip the sign bit of the fp16 scale (byte 1, bit 7) of half the blocks."""
+    q = q.copy()
+    flip = g.random(q.shape[:-1]) < 0.5
+    q[..., 1] ^= np.where(flip, 0x80, 0).astype(np.uint8)
+    return q
+
+
+def compare_per_token(L, g: dict):
+    K, E = L.spec.K, L.spec.E
+    logits_ref = oracle.router_logits(L.x, L.w_router)
+    scale = np.abs(logits_ref).max()
+    assert np.abs(g["logits"] - logits_ref).max() <= 1e-4 * max(scale, 1e-30)
+    ids_eff, w_ref, _ = parity.check_routing(L, g, logits_ref)
+    off, ss, sp = oracle.permute(ids_eff, E)
+    assert np.array_equal(g["offsets"], off) and np.array_equal(g["sorted_slots"], ss)
+    y_ref = oracle.expert_ffn(L.x, L.w_gate_up, L.w_down, K, off, ss)
+    out_ref = oracle.combine(y_ref, sp, ids_eff, w_ref, L.expert_scale)
+    assert np.all(np.isfinite(g["y_sorted"])) and np.all(np.isfinite(g["out"]))
+    errs = []
+    for p in range(y_ref.shape[0]):
+        m = np.abs(y_ref[p]).max()
+        d = np.abs(g["y_sorted"][p].astype(np.float64) - y_ref[p]).max()
+        assert d <= parity.TOL * m, "slot at sorted position %d: |dy| %g vs max|y| %g" % (p, d, m)
+        errs.append(d / m if m > 0 else 0.0)
+    for t in range(out_ref.shape[0]):
+        m = np.abs(out_ref[t]).max()
+        d = np.abs(g["out"][t].astype(np.float64) - out_ref[t]).max()
+        assert d <= parity.TOL * m, "token %d: |dout| %g vs max|out| %g" % (t, d, m)
+    return max(errs)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("case", CASES)
+def test_decode_1_token_fp32_edge(case, fused):
+    spec = synth.SPECS[1]
+    L = synth.make_layer(spec, seed=300 + CASES.index(case))
+    g = np.random.default_rng(7 + CASES.index(case))
+    L.x = shape_token(L.x[0], case, g)[None, :]
+    L.w_gate_up = negate_some_scales(L.w_gate_up, g)
+    L.w_down = negate_some_scales(L.w_down, g)
+    print("case: 1-token fp32 %s fused=%s" % (case, fused), flush=True)
+    gpu, _ = parity.run_gpu_layer(L, fused_route=fused)
+    print("  -> worst per-slot y error %.2e" % compare_per_token(L, gpu), flush=True)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_decode_8_tokens_bf16_edge(fused):
+    # one case per token, all in one 8-token batch
+    spec = synth.SPECS[2]
+    L = synth.make_layer(spec, seed=400)
+    g = np.random.default_rng(8)
+    xf = synth.normal_f32(g, (spec.T, spec.H), 0.0, 1.0)
+    rows = [shape_token(xf[t], CASES[t], g) for t in range(spec.T)]
+    L.x = synth.f32_to_bf16_bits(np.stack(rows))
+    L.w_gate_up = negate_some_scales(L.w_gate_up, g)
+    L.w_down = negate_some_scales(L.w_down, g)
+    print("case: 8-token bf16, one edge case per token, fused=%s" % fused, flush=True)
+    gpu, _ = parity.run_gpu_layer(L, fused_route=fused)
+    print("  -> worst per-slot y error %.2e" % compare_per_token(L, gpu), flush=True)

@@ -51,12 +51,46 @@ def test_decode_8_tokens_injected_uniform_logits():
     _run(L, logits_in=lg)
 
 
-def test_prefill_4096_tokens_sampled():
+def tile_covering_tokens(offsets: np.ndarray, sorted_slots: np.ndarray, K: int,
+                         tile: int = 128) -> np.ndarray:
+    """Tokens whose slots touch every (expert, slot tile) of the grouped GEMM:
+    greedily, each uncovered tile contributes the token of its last slot (the
+    ragged end of a partial tile), which also covers that token's other slots."""
+    N = sorted_slots.size
+    tile_of = np.empty(N, np.int64)
+    tiles = []
+    for e in range(offsets.size - 1):
+        for s0 in range(offsets[e], offsets[e + 1], tile):
+            tile_of[s0:min(s0 + tile, offsets[e + 1])] = len(tiles)
+            tiles.append((s0, min(s0 + tile, offsets[e + 1])))
+    pos_of_slot = np.empty(N, np.int64)
+    pos_of_slot[sorted_slots] = np.arange(N)
+    covered = np.zeros(len(tiles), bool)
+    chosen = []
+    for i, (s0, s1) in enumerate(tiles):
+        if covered[i]:
+            continue
+        t = int(sorted_slots[s1 - 1]) // K
+        chosen.append(t)
+        covered[tile_of[pos_of_slot[t * K:(t + 1) * K]]] = True
+    assert covered.all()
+    return np.unique(np.array(chosen))
+
+
+def test_prefill_4096_tokens_every_tile_sampled():
+    # every token's routing and permutation are compared; the expert outputs and
+    # the combined output on a token sample that touches every (expert, slot
+    # tile) of the grouped GEMM, plus the first and last token
     spec = synth.SPECS[3]
     L = synth.make_layer(spec)
-    sample = np.random.default_rng(3).choice(spec.T, size=12, replace=False)
-    sample = np.concatenate([[0, spec.T - 1], sample])
-    _run(L, token_sample=sample)
+    print("case: prefill-4096, GPU run", flush=True)
+    g, _ = parity.run_gpu_layer(L)
+    sample = tile_covering_tokens(g["offsets"], g["sorted_slots"], spec.K)
+    sample = np.unique(np.concatenate([[0, spec.T - 1], sample]))
+    ntiles = int(np.sum((np.diff(g["offsets"]) + 127) // 128))
+    print("  %d tokens cover all %d slot tiles" % (sample.size, ntiles), flush=True)
+    res = parity.check_layer(L, g, token_sample=sample)
+    print("  ->", res, flush=True)
 
 
 @pytest.mark.parametrize("T", [1, 2, 3, 7, 8, 33, 512])

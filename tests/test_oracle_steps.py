@@ -262,7 +262,8 @@ def torch_layer(L, K, logits_in=None):
             continue
         xe = x64[tok]
         h = torch.nn.functional.gelu(xe @ Wgu[:I].T, approximate="tanh") * (xe @ Wgu[I:].T)
-        h = h.float().double() if L.x.dtype == np.float32 else h
+        # h is materialised in the activation type (fp32, or bf16 via fp32)
+        h = h.float().double() if L.x.dtype == np.float32 else h.float().to(torch.bfloat16).double()
         y = h @ Wd.T
         c = w[tok, kk] * float(1) * torch.from_numpy(L.expert_scale.astype(np.float64))[e]
         out.index_add_(0, tok, c[:, None] * y)
@@ -325,3 +326,106 @@ def test_rmsnorm_against_torch():
     # zero rows stay zero (eps keeps the scale finite)
     z = oracle.rmsnorm(np.zeros((1, 256), np.uint16), w, 1e-6)
     assert np.all(z == 0)
+
+
+# ---- residual add and one block of the stack ----------------------------------
+def _bf16_table():
+    """Every finite bf16 value (decoded by torch) with its bit pattern, ascending;
+    -0 left out so that each value appears once."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = act_to_f64(bits)
+    keep = np.isfinite(vals) & (bits != 0x8000)
+    order = np.argsort(vals[keep], kind="stable")
+    return vals[keep][order], bits[keep][order]
+
+
+def nearest_even_bf16(s: np.ndarray) -> np.ndarray:
+    """Brute force: the bf16 nearest to each binary64 s, ties to the even pattern."""
+    vals, bits = _bf16_table()
+    i = np.clip(np.searchsorted(vals, s), 1, vals.size - 1)
+    lo, hi = vals[i - 1], vals[i]
+    dlo, dhi = s - lo, hi - s
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & ((bits[i] & 1) == 0))
+    return np.where(pick_hi, bits[i], bits[i - 1]).astype(np.uint16)
+
+
+def test_residual_is_nearest_even_bf16():
+    g = np.random.default_rng(21)
+    T, H = 12, 96
+    x = synth.f32_to_bf16_bits((g.standard_normal((T, H)) * 2).astype(np.float32))
+    out = g.standard_normal((T, H)) * np.exp(g.uniform(-12, 3, size=(T, H)))
+    xv = act_to_f64(x)
+    # exact ties: out = half a bf16 ulp of x (with x's sign), so x + out lies
+    # halfway between two bf16 values
+    ulp = np.ldexp(1.0, np.frexp(np.abs(xv))[1] - 8)
+    out[0] = np.sign(xv[0]) * ulp[0] / 2
+    out[1] = -np.sign(xv[1]) * ulp[1] / 4
+    got = oracle.residual(x, out)
+    assert np.array_equal(got, nearest_even_bf16(xv + out))
+    # out = 0 keeps x; x = 0 gives the rounding of out
+    assert np.array_equal(oracle.residual(x, np.zeros((T, H))), x)
+    z = np.zeros((T, H), np.uint16)
+    assert np.array_equal(oracle.residual(z, out), nearest_even_bf16(out))
+    # masked rows are untouched
+    m = np.zeros(T, np.uint8)
+    m[3] = 1
+    r = oracle.residual(x, out, token_mask=m)
+    assert np.array_equal(r[3], got[3]) and not r[np.arange(T) != 3].any()
+
+
+def stack_spec(T=5):
+    base = synth.SPECS[4]
+    return synth.LayerSpec(**{**base.__dict__, "H": 256, "E": 8, "K": 2, "I": 64, "T": T,
+                              "router_std": 1 / 16, "name": "tiny-stack"})
+
+
+def test_stack_layer_composes_norm_layer_residual():
+    spec = stack_spec()
+    L = synth.make_layer(spec, seed=31)
+    r = oracle.stack_layer(L.x, L.rms_w, spec.rms_eps, L.w_router, L.w_gate_up, L.w_down, spec.K,
+                           scale=L.expert_scale, bias=L.router_bias)
+    xhat = oracle.rmsnorm(L.x, L.rms_w, spec.rms_eps)
+    lay = oracle.moe_layer(xhat, L.w_router, L.w_gate_up, L.w_down, spec.K, scale=L.expert_scale,
+                           bias=L.router_bias)
+    assert np.array_equal(r["xhat"], xhat)
+    assert np.array_equal(r["ids"], lay["ids"])
+    assert np.array_equal(r["out"], lay["out"])
+    assert np.array_equal(r["x_next"], oracle.residual(L.x, lay["out"]))
+
+
+def test_stack_layer_against_torch_composition():
+    spec = stack_spec(T=6)
+    L = synth.make_layer(spec, seed=33)
+    r = oracle.stack_layer(L.x, L.rms_w, spec.rms_eps, L.w_router, L.w_gate_up, L.w_down, spec.K,
+                           scale=L.expert_scale, bias=L.router_bias)
+    x64 = torch.from_numpy(act_to_f64(L.x))
+    xh = torch.nn.functional.rms_norm(x64, (spec.H,), weight=torch.from_numpy(
+        L.rms_w.astype(np.float64)), eps=spec.rms_eps)
+    xhb = xh.float().to(torch.bfloat16)
+    L2 = synth.LayerInputs(spec, spec.T, xhb.view(torch.int16).numpy().view(np.uint16).copy(),
+                           L.w_router, L.router_bias, L.w_gate_up, L.w_down, L.expert_scale)
+    _, ids, _, out = torch_layer(L2, spec.K)
+    xn = (x64 + torch.from_numpy(out)).float().to(torch.bfloat16)
+    xn = xn.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(r["ids"], ids)
+    # torch rounds fp64 -> fp32 -> bf16, the oracle fp64 -> bf16 once: equal
+    # except for double-rounding ties, one ulp apart
+    diff = np.abs(r["x_next"].astype(np.int32) - xn.astype(np.int32))
+    assert diff.max() <= 1 and (diff > 0).mean() < 1e-2
+
+
+def test_stack_layer_degenerate_inputs():
+    spec = stack_spec(T=3)
+    L = synth.make_layer(spec, seed=35)
+    # x = 0: the norm stays finite (eps), the experts see zeros, so x stays 0
+    z = np.zeros_like(L.x)
+    r = oracle.stack_layer(z, L.rms_w, spec.rms_eps, L.w_router, L.w_gate_up, L.w_down, spec.K,
+                           scale=L.expert_scale, bias=L.router_bias)
+    assert not r["xhat"].any() and not r["x_next"].any() and np.all(r["out"] == 0)
+    # zero expert scales d: every expert weight is 0, so the block returns x
+    gu, dn = L.w_gate_up.copy(), L.w_down.copy()
+    gu[..., 0:2] = 0
+    dn[..., 0:2] = 0
+    r = oracle.stack_layer(L.x, L.rms_w, spec.rms_eps, L.w_router, gu, dn, spec.K,
+                           scale=L.expert_scale, bias=L.router_bias)
+    assert np.array_equal(r["x_next"], L.x)
