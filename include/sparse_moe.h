@@ -58,6 +58,7 @@ extern "C" {
 #define MOE_MAX_H 4096
 #define MOE_MAX_I 4096
 #define MOE_MAX_LINEAR_ROWS 65536
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20) /* static workspace per GPU, see below */
 
 typedef enum {
     MOE_OK = 0,
@@ -66,7 +67,8 @@ typedef enum {
     MOE_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
     MOE_ERR_UNSUPPORTED = 4, /* unknown dtype or option */
     MOE_ERR_WORKSPACE = 5,   /* workspace missing or too small */
-    MOE_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+    MOE_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
+    MOE_ERR_SCRATCH = 7      /* needs more than the no-allocation entry point's scratch */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -177,6 +179,29 @@ moe_status moe_expert_ffn_q4_0(const void* x, int x_dt, int64_t T, int32_t H,
                                int32_t K, const int32_t* expert_offsets,
                                const int32_t* sorted_slots, float* y_sorted, void* ws,
                                size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn_q4_0 without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, kernels and results as
+ * moe_expert_ffn_q4_0 (bitwise), with the workspace taken from a static device
+ * array of MOE_NOALLOC_SCRATCH_BYTES (16 MiB) that the library holds once per
+ * GPU until the process ends.  Nothing is allocated: the array's address is
+ * looked up once per device (hipGetSymbolAddress) and kept.
+ *  - Returns MOE_ERR_SCRATCH, enqueueing nothing, when
+ *    moe_expert_ffn_q4_0_workspace_bytes(T, K, H, I, E, x_dt) exceeds the
+ *    array (at the Gemma shape: about 934 tokens on the bf16 MFMA path; every
+ *    decode batch of fewer than 64 tokens fits).
+ *  - Every call on one GPU shares that GPU's array, and the array keeps the
+ *    last call's contents (the workspace needs no initialisation).  Calls
+ *    whose execution overlaps on one GPU (other streams, other threads) race
+ *    on it: order them on one stream.
+ */
+moe_status moe_expert_ffn_q4_0_noalloc(const void* x, int x_dt, int64_t T, int32_t H,
+                                       const void* w_gate_up, const void* w_down, int32_t I,
+                                       int32_t E, int32_t K, const int32_t* expert_offsets,
+                                       const int32_t* sorted_slots, float* y_sorted,
+                                       void* stream);
 
 /*
  * Plain Q4_0 linear layer (model card table "What is inside": the Q, K and V

@@ -21,7 +21,8 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_MAX_E, MOE_MAX_K = 256, 16
 
 _STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN",
-           4: "MOE_ERR_UNSUPPORTED", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_HIP"}
+           4: "MOE_ERR_UNSUPPORTED", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_HIP",
+           7: "MOE_ERR_SCRATCH"}
 
 # every function the header declares, with its ctypes signature
 _P, _I32, _I64, _SZ, _F32 = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_float
@@ -37,6 +38,8 @@ SIGNATURES = {
     "moe_expert_ffn_q4_0_workspace_bytes": ([_I64, _I32, _I32, _I32, _I32, C.c_int], _SZ),
     "moe_expert_ffn_q4_0": ([_P, C.c_int, _I64, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P,
                              _SZ, _P], C.c_int),
+    "moe_expert_ffn_q4_0_noalloc": ([_P, C.c_int, _I64, _I32, _P, _P, _I32, _I32, _I32, _P, _P,
+                                     _P, _P], C.c_int),
     "moe_combine": ([_P, _P, _P, _P, _P, _I64, _I32, _I32, _P, C.c_int, _P, _P, C.c_int, _P],
                     C.c_int),
     "moe_rmsnorm": ([_P, C.c_int, _P, _F32, _I64, _I32, _P, C.c_int, _P], C.c_int),
@@ -195,6 +198,29 @@ def moe_expert_ffn_q4_0(x: torch.Tensor, w_gate_up: torch.Tensor, w_down: torch.
                                    K, _ptr(expert_offsets), _ptr(sorted_slots), _ptr(y_sorted),
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "moe_expert_ffn_q4_0")
+
+
+def moe_expert_ffn_q4_0_noalloc(x: torch.Tensor, w_gate_up: torch.Tensor, w_down: torch.Tensor,
+                                K: int, expert_offsets: torch.Tensor, sorted_slots: torch.Tensor,
+                                y_sorted: torch.Tensor, stream=None):
+    """moe_expert_ffn_q4_0 with the library's static per-GPU scratch as workspace."""
+    T, H = x.shape
+    E = w_gate_up.shape[0]
+    I = w_gate_up.shape[1] // 2
+    _dev(x, "x")
+    _dev(w_gate_up, "w_gate_up", torch.uint8)
+    _dev(w_down, "w_down", torch.uint8)
+    _dev(expert_offsets, "expert_offsets", torch.int32)
+    _dev(sorted_slots, "sorted_slots", torch.int32)
+    _dev(y_sorted, "y_sorted", torch.float32)
+    if w_gate_up.numel() != E * 2 * I * (H // 32) * 18 or w_down.numel() != E * H * (I // 32) * 18:
+        raise ValueError("Q4_0 weight sizes disagree with [E][2I][H/32][18] / [E][H][I/32][18]")
+    if tuple(y_sorted.shape) != (T * K, H):
+        raise ValueError("y_sorted must be [T*K, H]")
+    _check(lib.moe_expert_ffn_q4_0_noalloc(_ptr(x), act_dtype(x), T, H, _ptr(w_gate_up),
+                                           _ptr(w_down), I, E, K, _ptr(expert_offsets),
+                                           _ptr(sorted_slots), _ptr(y_sorted), _stream(stream)),
+           "moe_expert_ffn_q4_0_noalloc")
 
 
 def moe_linear_q4_0(x: torch.Tensor, w: torch.Tensor, y: Optional[torch.Tensor] = None,

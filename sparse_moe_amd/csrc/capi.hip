@@ -2,8 +2,14 @@
 // dispatch to the gfx950 kernels.  Nothing here allocates, frees or
 // synchronises; every call only enqueues on the caller's stream.
 #include <algorithm>
+#include <mutex>
 
 #include "kernels.h"
+
+// Workspace of moe_expert_ffn_q4_0_noalloc: one copy per GPU, held until the
+// process ends.  In host code `scratch` only names the symbol; its device
+// address on each GPU comes from hipGetSymbolAddress (scratch_address below).
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -24,6 +30,32 @@ moe_status check_dim(int32_t D, int32_t maxD) {
     return (D < 32 || D % 32 != 0 || D > maxD) ? MOE_ERR_SHAPE : MOE_OK;
 }
 
+// Device address of `scratch` on the device that owns `stream` (the current
+// device for the null stream), looked up once per device with that device
+// current and kept.
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[SCRATCH_MAX_DEVICES];
+
+moe_status scratch_address(hipStream_t stream, void** out) {
+    int cur = 0, dev = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return MOE_ERR_HIP;
+    dev = cur;
+    if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return MOE_ERR_HIP;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) return MOE_ERR_HIP;
+        if (e != hipSuccess || !p) return MOE_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -37,6 +69,9 @@ const char* moe_status_string(int status) {
         case MOE_ERR_UNSUPPORTED: return "unsupported dtype or option";
         case MOE_ERR_WORKSPACE: return "workspace missing or too small";
         case MOE_ERR_HIP: return "the HIP runtime reported a launch error";
+        case MOE_ERR_SCRATCH:
+            return "the call needs more workspace than the static scratch of the "
+                   "no-allocation entry point holds (MOE_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
@@ -170,6 +205,26 @@ moe_status moe_expert_ffn_q4_0(const void* x, int x_dt, int64_t T, int32_t H,
                                            (const uint8_t*)w_down, I, E, K, (int)(T * K),
                                            expert_offsets, sorted_slots, ws, y_sorted,
                                            (hipStream_t)stream));
+}
+
+moe_status moe_expert_ffn_q4_0_noalloc(const void* x, int x_dt, int64_t T, int32_t H,
+                                       const void* w_gate_up, const void* w_down, int32_t I,
+                                       int32_t E, int32_t K, const int32_t* expert_offsets,
+                                       const int32_t* sorted_slots, float* y_sorted,
+                                       void* stream) {
+    moe_status s = check_ekh(T, K, E);
+    if (s != MOE_OK) return s;
+    if ((s = check_dim(H, MOE_MAX_H)) != MOE_OK || (s = check_dim(I, MOE_MAX_I)) != MOE_OK) return s;
+    if (!dtype_ok(x_dt)) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (moe_expert_ffn_q4_0_workspace_bytes(T, K, H, I, E, x_dt) > MOE_NOALLOC_SCRATCH_BYTES)
+        return MOE_ERR_SCRATCH;
+    if (!x || !w_gate_up || !w_down || !expert_offsets || !sorted_slots || !y_sorted)
+        return MOE_ERR_NULL;
+    void* ws = nullptr;
+    if ((s = scratch_address((hipStream_t)stream, &ws)) != MOE_OK) return s;
+    return moe_expert_ffn_q4_0(x, x_dt, T, H, w_gate_up, w_down, I, E, K, expert_offsets,
+                               sorted_slots, y_sorted, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t moe_linear_q4_0_workspace_bytes(int64_t T, int32_t H, int32_t R, int x_dt) {

@@ -38,8 +38,8 @@ def test_exports_every_declared_function():
 
 
 def test_status_strings():
-    for s in range(7):
-        assert lib.moe_status_string(s)
+    for s in range(8):
+        assert lib.moe_status_string(s) != b"unknown status"
     assert lib.moe_status_string(99) == b"unknown status"
 
 
@@ -103,6 +103,22 @@ def test_ffn_validation_and_workspace():
     assert f(A, 1, 4, 2816, MIS, A, 704, 128, 8, A, A, A, A, ws, None) == ALIGN
     assert f(A, 3, 4, 2816, A, A, 704, 128, 8, A, A, A, A, ws, None) == UNSUP
     assert f(None, 1, 0, 2816, None, None, 704, 128, 8, None, None, None, None, 0, None) == OK
+
+
+def test_ffn_noalloc_validation():
+    f = lib.moe_expert_ffn_q4_0_noalloc
+    SCRATCH = 7
+    # (x, x_dt, T, H, w_gu, w_dn, I, E, K, offsets, sorted, y, stream)
+    assert f(A, 1, 4096, 2816, A, A, 704, 128, 8, A, A, A, None) == SCRATCH   # prefill: too big
+    assert f(A, 1, 1024, 2816, A, A, 704, 128, 8, A, A, A, None) == SCRATCH
+    assert f(None, 1, 8, 2816, A, A, 704, 128, 8, A, A, A, None) == NULL      # fits, x missing
+    assert f(A, 1, 8, 2816, A, A, 700, 128, 8, A, A, A, None) == SHAPE
+    assert f(A, 4, 8, 2816, A, A, 704, 128, 8, A, A, A, None) == UNSUP
+    assert f(None, 1, 0, 2816, None, None, 704, 128, 8, None, None, None, None) == OK
+    # every decode batch below 64 tokens fits; 934 bf16 tokens at the Gemma shape do
+    big = lib.moe_expert_ffn_q4_0_workspace_bytes
+    assert big(63, 8, 2816, 704, 128, 0) <= 16 << 20
+    assert big(934, 8, 2816, 704, 128, 1) <= 16 << 20 < big(935, 8, 2816, 704, 128, 1)
 
 
 def test_combine_and_rmsnorm_validation():
