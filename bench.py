@@ -43,7 +43,10 @@ def parse():
     p.add_argument("--config", type=int, default=1,
                    help="workload: 0 tiny, 1 decode 1 token, 2 decode 8 tokens, 3 prefill 4096, "
                         "4 stack of 30 layers x 512 tokens")
-    p.add_argument("--sets", type=int, default=0, help="weight sets rotated (0: auto)")
+    p.add_argument("--sets", type=int, default=0,
+                   help="weight sets in distinct memory (0: 32 for decode, 4 for prefill)")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="default workload only: leave out the nested 4,096-token prefill leg")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -149,26 +152,60 @@ def summarize_stats(args):
     print("wrote", out_md)
 
 
+def host_info():
+    """Cores this process may use, and the host CPU model."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"host_cores": len(os.sched_getaffinity(0)), "host_cores_total": os.cpu_count(),
+            "cpu_model": model}
+
+
+class one_core:
+    """Pin this process to one of its cores while the oracle runs."""
+
+    def __enter__(self):
+        self.saved = os.sched_getaffinity(0)
+        self.core = min(self.saved)
+        os.sched_setaffinity(0, {self.core})
+        return self
+
+    def __exit__(self, *exc):
+        os.sched_setaffinity(0, self.saved)
+
+
 def cpu_baseline(spec, seconds: float):
-    """The oracle as it stands, single-threaded, on a bounded token sample."""
+    """The oracle as it stands, single-threaded and pinned to one core, on a
+    bounded token sample."""
     import oracle
     from sparse_moe_amd import synth
     if spec.layers > 1:
         return cpu_baseline_stack(spec, seconds)
+    info = host_info()
     L = synth.make_layer(spec, T=1)
     xs = synth.activations(spec, 64, spec.seed + 77)
-    n, t0 = 0, time.perf_counter()
-    while n < xs.shape[0]:
-        oracle.moe_layer(xs[n:n + 1], L.w_router, L.w_gate_up, L.w_down, spec.K,
-                         scale=L.expert_scale, bias=L.router_bias)
-        n += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
+    oracle.lib()
+    with one_core() as pin:
+        n, t0 = 0, time.perf_counter()
+        while n < xs.shape[0]:
+            oracle.moe_layer(xs[n:n + 1], L.w_router, L.w_gate_up, L.w_down, spec.K,
+                             scale=L.expert_scale, bias=L.router_bias)
+            n += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "pinned_core": pin.core, **info,
             "sample": "%d tokens of the %s layer, one at a time, full layer per token "
                       "(router over all experts, top-%d, %d expert FFNs, combine), "
-                      "single-threaded binary64 C oracle" % (n, spec.name, spec.K, spec.K)}
+                      "single-threaded binary64 C oracle pinned to one core"
+                      % (n, spec.name, spec.K, spec.K)}
 
 
 def bench_stack(args, spec):
@@ -312,26 +349,238 @@ def cpu_baseline_stack(spec, seconds: float):
     from sparse_moe_amd import synth
     Ls = [synth.make_layer(spec, seed=synth.stack_layer_seed(l), T=1, with_x=False) for l in range(2)]
     xs = synth.activations(spec, 64, spec.seed + 77)
-    n, t0 = 0, time.perf_counter()
-    while n < xs.shape[0]:
-        x = xs[n:n + 1]
-        for L in Ls:
-            xh = oracle.rmsnorm(x, L.rms_w, spec.rms_eps)
-            r = oracle.moe_layer(xh, L.w_router, L.w_gate_up, L.w_down, spec.K,
-                                 scale=L.expert_scale, bias=L.router_bias)
-            xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-            x = synth.f32_to_bf16_bits((xf + r["out"]).astype(np.float32))
-        n += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
+    info = host_info()
+    oracle.lib()
+    with one_core() as pin:
+        n, t0 = 0, time.perf_counter()
+        while n < xs.shape[0]:
+            x = xs[n:n + 1]
+            for L in Ls:
+                x = oracle.stack_layer(x, L.rms_w, spec.rms_eps, L.w_router, L.w_gate_up,
+                                       L.w_down, spec.K, scale=L.expert_scale,
+                                       bias=L.router_bias)["x_next"]
+            n += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
     per_token_layer = dt / (n * len(Ls))
     return {"value": 1.0 / (per_token_layer * spec.layers), "unit": "tokens/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "pinned_core": pin.core, **info,
             "sample": "%d tokens one at a time through 2 of the %d layers (RMSNorm, router with "
                       "Zipf prior over all experts, top-%d, %d expert FFNs, combine, residual), "
-                      "single-threaded binary64 C oracle; rate scaled to %d layers"
-                      % (n, spec.layers, spec.K, spec.K, spec.layers)}
+                      "single-threaded binary64 C oracle pinned to one core; rate scaled to %d "
+                      "layers" % (n, spec.layers, spec.K, spec.K, spec.layers)}
+
+
+def mfma_path(act: str, T: int, H: int, I: int) -> bool:
+    """Whether moe_expert_ffn_q4_0 takes its bf16 MFMA path (the library's
+    dispatch rule, include/sparse_moe.h): bf16 activations, at least 64 tokens,
+    H and I multiples of 64."""
+    return act == "bf16" and T >= 64 and H % 64 == 0 and I % 64 == 0
+
+
+def dev_tensor(a, dev="cuda"):
+    import numpy as np
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(a).to(dev)
+
+
+def weight_sets(spec, n: int, dev="cuda"):
+    """n weight sets of one layer, each in its own device memory: a seeded
+    synthetic layer, and n - 1 copies with the experts (and the router rows,
+    scales and prior that belong to them) stored in a seeded random order.  A
+    token routes to the same expert contents in every set, at different
+    addresses, so no set finds another's experts in a cache."""
+    import torch
+    from sparse_moe_amd import synth
+    L = synth.make_layer(spec, seed=spec.seed + 1000, with_x=False)
+    base = dict(wr=dev_tensor(L.w_router, dev), gu=dev_tensor(L.w_gate_up, dev),
+                dn=dev_tensor(L.w_down, dev), sc=dev_tensor(L.expert_scale, dev),
+                bias=None if L.router_bias is None else dev_tensor(L.router_bias, dev))
+    del L
+    sets = [base]
+    gen = torch.Generator().manual_seed(spec.seed + 2000)
+    for _ in range(1, n):
+        perm = torch.randperm(spec.E, generator=gen).to(dev)
+        sets.append({k: None if v is None else v.index_select(0, perm).contiguous()
+                     for k, v in base.items()})
+    return sets
+
+
+def bench_layer(spec, steps: int, warmup: int, nsets: int, cpu_seconds: float = 0.0):
+    """One routed-MoE layer (routing, expert FFN, combine): K timed steps, each a
+    replay of one of G HIP graphs, graph r running weight set r mod nsets on
+    token batch r, so consecutive uses of a set are nsets graphs apart and a
+    cycle touches G different routings; then the expert-FFN call alone, timed
+    over replays of one graph of F calls, call f on set f with the routing of
+    batch f."""
+    import torch
+    from sparse_moe_amd import binding, synth
+    T, H, E, K, I = spec.T, spec.H, spec.E, spec.K, spec.I
+    act = torch.float32 if spec.act == "f32" else torch.bfloat16
+    sets = weight_sets(spec, nsets)
+    G = nsets * (2 if T <= 64 else 1)
+    F = nsets
+    xpool = dev_tensor(synth.activations(spec, T * G, spec.seed + 7)).view(G, T, H)
+    bufs = binding.LayerBuffers(T, H, I, E, K, act)
+
+    def route(r, si=None):
+        s = sets[r % nsets if si is None else si]
+        binding.moe_route(xpool[r], s["wr"], bufs.logits, bufs.topk_ids, bufs.topk_w, bufs.offsets,
+                          bufs.sorted_slots, bufs.slot_pos, bufs.ws_route, logit_bias=s["bias"])
+
+    def step(r, si=None):
+        s = sets[r % nsets if si is None else si]
+        route(r, si)
+        binding.moe_expert_ffn_q4_0(xpool[r], s["gu"], s["dn"], K, bufs.offsets,
+                                    bufs.sorted_slots, bufs.y_sorted, bufs.ws_ffn)
+        binding.moe_combine(bufs.y_sorted, bufs.slot_pos, bufs.topk_ids, bufs.topk_w, s["sc"],
+                            out_f32=bufs.out)
+
+    # routing of every batch (distinct experts for the algorithmic bytes; the FFN
+    # timing graph's per-call routing)
+    distinct, routes = [], []
+    for r in range(G):
+        route(r)
+        torch.cuda.synchronize()
+        distinct.append(int((bufs.offsets[1:] - bufs.offsets[:-1] > 0).sum().item()))
+        if r < F:
+            routes.append((bufs.offsets.clone(), bufs.sorted_slots.clone()))
+    # every set holds the same experts in another order: one batch's output is the
+    # same, bit for bit, whatever the set
+    step(0)
+    torch.cuda.synchronize()
+    out0 = bufs.out.clone()
+    if nsets > 1:
+        step(0, si=nsets - 1)
+        torch.cuda.synchronize()
+        assert torch.equal(out0, bufs.out), "weight sets disagree"
+    for r in range(warmup):
+        step(r % G)
+    torch.cuda.synchronize()
+    graphs = []
+    for r in range(G):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(r)
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % G].replay()
+    torch.cuda.synchronize()
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out0, bufs.out), "graph replay differs from eager execution"
+    if nsets > 1 and G > nsets:
+        graphs[nsets].replay()          # batch nsets on set 0, ...
+        torch.cuda.synchronize()
+        out_n = bufs.out.clone()
+        step(nsets)
+        torch.cuda.synchronize()
+        assert torch.equal(out_n, bufs.out)
+
+    # timed region: K steps as graph replays
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record()
+    for i in range(steps):
+        graphs[i % G].replay()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = t_start.elapsed_time(t_end) / steps
+
+    # dominant kernel: the expert-FFN call, with HIP events on its stream around
+    # replays of one graph of F calls (no host launch gap timed)
+    g_ffn = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_ffn):
+        for f in range(F):
+            s = sets[f]
+            binding.moe_expert_ffn_q4_0(xpool[f], s["gu"], s["dn"], K, routes[f][0], routes[f][1],
+                                        bufs.y_sorted, bufs.ws_ffn)
+    g_ffn.replay()
+    torch.cuda.synchronize()
+    reps = max(2, steps // F)
+    ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev_a.record()
+    for _ in range(reps):
+        g_ffn.replay()
+    ev_b.record()
+    torch.cuda.synchronize()
+    ffn_ms = ev_a.elapsed_time(ev_b) / (reps * F)
+
+    expert_bytes = Q4_0_EXPERT_BYTES(H, I)
+    asz = 4 if act == torch.float32 else 2
+    N = T * K
+    # algorithmic bytes: the distinct experts' Q4_0 bytes, x, h written and read,
+    # y written (FFN call); plus the router, scales and output (layer)
+    ffn_bytes = [d * expert_bytes + T * H * asz + N * I * asz * 2 + N * H * 4
+                 for d in distinct[:F]]
+    ffn_bytes_mean = sum(ffn_bytes) / F
+    layer_bytes = sum(d * expert_bytes + E * H * 4 + T * H * asz + E * 4 + T * H * 4
+                      for d in distinct) / G
+    layer_hbm = layer_bytes / (ms_step * 1e-3) / 1e9
+    ffn_flops = N * 6.0 * H * I          # per slot 2 (2I H) + 2 (H I)
+    layer_tflops = ffn_flops / (ms_step * 1e-3) / 1e12
+    if mfma_path(spec.act, T, H, I):
+        achieved = ffn_flops / (ffn_ms * 1e-3) / 1e12
+        roofline = {"kernel": "moe_expert_ffn_q4_0 (activation prep, gate/up and down bf16 MFMA "
+                              "grouped GEMM launches)",
+                    "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                    "flops_per_launch": ffn_flops, "avg_launch_us": ffn_ms * 1e3}
+        dtype = "q4_0 x bf16 (exact bf16 MFMA products, fp32 accumulate)"
+    else:
+        achieved = ffn_bytes_mean / (ffn_ms * 1e-3) / 1e9
+        roofline = {"kernel": "moe_expert_ffn_q4_0 (gate/up then down Q4_0 GEMV launches)",
+                    "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                    "bytes_per_launch": ffn_bytes_mean, "avg_launch_us": ffn_ms * 1e3}
+        dtype = ("q4_0 x %s (activation blocks rounded to 15-bit fixed point, exact int4 digit "
+                 "products, fp32 accumulate)" % spec.act)
+    tr = stored_traffic(spec.name)
+    if tr is not None:
+        roofline["traffic"] = tr["traffic_bytes"]
+        roofline["traffic_fetch"] = tr["fetch_bytes"]
+        roofline["traffic_write"] = tr["write_bytes"]
+    res = {
+        "metric": METRIC,
+        "value": T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded; random-init Q4_0 experts; %d weight sets in distinct memory, "
+                "%d token batches)" % (nsets, G),
+        "config": {"workload": "%s: Gemma-4-26B-A4B-shaped routed-MoE layer, T=%d, H=%d, E=%d, "
+                               "top-%d, I=%d, Q4_0 experts, %s activations"
+                               % (spec.name, T, H, E, K, I, spec.act),
+                   "tokens_per_step": T, "weight_sets": nsets, "graphs": G,
+                   "distinct_experts_per_step_mean": sum(distinct) / G,
+                   "distinct_experts_per_step_min_max": [min(distinct), max(distinct)],
+                   "layer_hbm_gbs": layer_hbm, "layer_hbm_frac": layer_hbm / HBM_PEAK_GBS,
+                   "layer_expert_tflops": layer_tflops,
+                   "layer_mfma_frac": layer_tflops / BF16_PEAK_TFLOPS,
+                   "wall_s": wall,
+                   "timing": "K steps, step i a replay of HIP graph i mod %d (set i mod %d, batch "
+                             "i mod %d); the FFN call over replays of one graph of %d calls on "
+                             "%d sets and routings" % (G, nsets, G, F, F)},
+        "roofline": roofline,
+    }
+    if cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(spec, cpu_seconds)
+    del graphs, g_ffn, sets, xpool, bufs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -345,7 +594,7 @@ def main():
               "(the layer would shard over experts, one process per GPU)", file=sys.stderr)
         sys.exit(2)
     import torch
-    from sparse_moe_amd import binding, synth
+    from sparse_moe_amd import synth
     torch.cuda.set_device(0)
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
@@ -357,169 +606,14 @@ def main():
     spec = synth.SPECS[args.config]
     if spec.layers > 1:
         return bench_stack(args, spec)
-    T, H, E, K, I = spec.T, spec.H, spec.E, spec.K, spec.I
-    act = torch.float32 if spec.act == "f32" else torch.bfloat16
-    dev = "cuda"
-
-    def dev_t(a):
-        import numpy as np
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(a).to(dev)
-
-    expert_bytes = Q4_0_EXPERT_BYTES(H, I)
-    layer_bytes = E * expert_bytes
-    nsets = args.sets or max(1, min(16, -(-3 * 1024 ** 3 // layer_bytes)))
-    sets = []
-    for r in range(nsets):
-        L = synth.make_layer(spec, seed=spec.seed + 1000 * r, with_x=False)
-        sets.append(dict(wr=dev_t(L.w_router), gu=dev_t(L.w_gate_up), dn=dev_t(L.w_down),
-                         sc=dev_t(L.expert_scale),
-                         bias=None if L.router_bias is None else dev_t(L.router_bias)))
-        del L
-    npool = 16
-    xpool = dev_t(synth.activations(spec, T * npool, spec.seed + 7)).view(npool, T, H)
-    bufs = binding.LayerBuffers(T, H, I, E, K, act)
-
-    def step(i, ev_a=None, ev_b=None):
-        s = sets[i % nsets]
-        x = xpool[i % npool]
-        binding.moe_route(x, s["wr"], bufs.logits, bufs.topk_ids, bufs.topk_w, bufs.offsets,
-                          bufs.sorted_slots, bufs.slot_pos, bufs.ws_route, logit_bias=s["bias"])
-        if ev_a is not None:
-            ev_a.record()
-        binding.moe_expert_ffn_q4_0(x, s["gu"], s["dn"], K, bufs.offsets, bufs.sorted_slots,
-                                    bufs.y_sorted, bufs.ws_ffn)
-        if ev_b is not None:
-            ev_b.record()
-        binding.moe_combine(bufs.y_sorted, bufs.slot_pos, bufs.topk_ids, bufs.topk_w, s["sc"],
-                            out_f32=bufs.out)
-
-    # distinct experts per step (for the algorithmic bytes of the FFN)
-    distinct = []
-    for i in range(nsets):
-        step(i)
-        torch.cuda.synchronize()
-        distinct.append(int((bufs.offsets[1:] - bufs.offsets[:-1] > 0).sum().item()))
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # one HIP graph per weight set: a step is launch-bound without it
-    graphs = []
-    for r in range(nsets):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(r)
-        graphs.append(g)
-    for i in range(args.warmup):
-        graphs[i % nsets].replay()
-    torch.cuda.synchronize()
-    # graph replays must reproduce the eager result bit for bit
-    graphs[0].replay()
-    torch.cuda.synchronize()
-    out_graph = bufs.out.clone()
-    step(0)
-    torch.cuda.synchronize()
-    assert torch.equal(out_graph, bufs.out), "graph replay differs from eager execution"
-
-    # timed region: K steps as graph replays
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    t_start.record()
-    for i in range(args.steps):
-        graphs[i % nsets].replay()
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
-
-    # dominant kernel: the expert-FFN call, timed with HIP events on its stream
-    # around replays of one HIP graph of F calls, each on the next weight set
-    # (the routing of step 0 for all: the same expert ids, different memory), so
-    # no call finds its experts in the memory-side cache and no host launch gap
-    # is timed; per call = elapsed / calls
-    step(0)
-    torch.cuda.synchronize()
-    F = max(1, min(nsets, 8))
-    g_ffn = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_ffn):
-        for f in range(F):
-            s = sets[f % nsets]
-            binding.moe_expert_ffn_q4_0(xpool[0], s["gu"], s["dn"], K, bufs.offsets,
-                                        bufs.sorted_slots, bufs.y_sorted, bufs.ws_ffn)
-    g_ffn.replay()
-    torch.cuda.synchronize()
-    reps = max(1, args.steps // F)
-    ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev_a.record()
-    for _ in range(reps):
-        g_ffn.replay()
-    ev_b.record()
-    torch.cuda.synchronize()
-    ffn_avg_ms = ev_a.elapsed_time(ev_b) / (reps * F)
-
-    # algorithmic bytes of one expert-FFN call (dominant kernel): the distinct
-    # experts of the routing the timed calls use
-    asz = 4 if act == torch.float32 else 2
-    N = T * K
-    d_avg = distinct[0]
-    ffn_bytes = (d_avg * expert_bytes + T * H * asz + N * I * asz * 2 + N * H * 4)
-    achieved = ffn_bytes / (ffn_avg_ms * 1e-3) / 1e9
-    layer_hbm = (d_avg * expert_bytes + E * H * 4 + T * H * asz + E * 4 + T * H * 4) / (ms_step * 1e-3) / 1e9
-    # algorithmic FLOPs of the expert FFN: per slot 2 * (2I * H) + 2 * (H * I)
-    ffn_flops = N * 6.0 * H * I
-    mfma_path = spec.act == "bf16" and T >= 64
-    if mfma_path:
-        roofline = {"kernel": "moe_expert_ffn_q4_0 (activation prep, gate/up and down bf16 MFMA "
-                              "grouped GEMM launches)",
-                    "bound": "mfma", "achieved": ffn_flops / (ffn_avg_ms * 1e-3) / 1e12,
-                    "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": ffn_flops / (ffn_avg_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                    "traffic": None, "flops_per_launch": ffn_flops, "avg_launch_us": ffn_avg_ms * 1e3}
-        dtype = "q4_0 x bf16 (exact bf16 MFMA products, fp32 accumulate)"
-    else:
-        roofline = {"kernel": "moe_expert_ffn_q4_0 (gate/up then down Q4_0 GEMV launches)",
-                    "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                    "bytes_per_launch": ffn_bytes, "avg_launch_us": ffn_avg_ms * 1e3}
-        dtype = "q4_0 x %s (int4 digit products, fp32 accumulate)" % spec.act
-    layer_tflops = ffn_flops / (ms_step * 1e-3) / 1e12
-    tr = stored_traffic(spec.name)
-    if tr is not None:
-        roofline["traffic"] = tr["traffic_bytes"]
-        roofline["traffic_fetch"] = tr["fetch_bytes"]
-        roofline["traffic_write"] = tr["write_bytes"]
-
-    res = {
-        "metric": METRIC,
-        "value": T * args.steps / (ms_total * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": dtype,
-        "data": "synthetic (seeded; random-init Q4_0 experts, %d weight sets rotated)" % nsets,
-        "config": {"workload": "%s: Gemma-4-26B-A4B-shaped routed-MoE layer, T=%d, H=%d, E=%d, "
-                               "top-%d, I=%d, Q4_0 experts, %s activations"
-                               % (spec.name, T, H, E, K, I, spec.act),
-                   "tokens_per_step": T, "weight_sets": nsets,
-                   "distinct_experts_per_step": d_avg,
-                   "layer_hbm_gbs": layer_hbm, "layer_hbm_frac": layer_hbm / HBM_PEAK_GBS,
-                   "layer_expert_tflops": layer_tflops,
-                   "layer_mfma_frac": layer_tflops / BF16_PEAK_TFLOPS,
-                   "wall_s": wall, "timing": "K steps replayed from one HIP graph per weight set; the FFN call timed over graph replays of 8 calls on rotating weight sets"},
-        "roofline": roofline,
-    }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(spec, args.cpu_seconds)
+    nsets = args.sets or (32 if spec.T <= 64 else 4)
+    cpu_s = 0.0 if args.no_cpu_baseline else args.cpu_seconds
+    res = bench_layer(spec, args.steps, args.warmup, nsets, cpu_s)
+    if args.config == 1 and not args.no_prefill:
+        # the other half of the metric: the 4,096-token prefill, MFMA-bound
+        p = bench_layer(synth.SPECS[3], max(5, args.steps // 10), max(2, args.warmup // 4), 4)
+        res["prefill"] = {k: p[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup",
+                                            "dtype", "data", "config", "roofline")}
     print(json.dumps(res), flush=True)
 
 
