@@ -28,10 +28,11 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 METRIC = "MoE-layer tokens/sec at 1 MI355X; decode HBM GB/s %peak, prefill MFMA %peak"
 Q4_0_EXPERT_BYTES = lambda H, I: 3 * H * I // 32 * 18   # [gate; up] + down
-# sources of the expert-FFN kernels: stored PMC traffic is reported only while
-# they are unchanged
-FFN_SOURCES = ("sparse_moe_amd/csrc/ffn_gemv.hip", "sparse_moe_amd/csrc/ffn_mfma.hip",
-               "sparse_moe_amd/csrc/common.h", "sparse_moe_amd/csrc/kernels.h")
+# stored PMC traffic is reported only while the kernel sources are unchanged
+KERNEL_SOURCE_DIR = "sparse_moe_amd/csrc"
+# kernels of the call the roofline times: the decode layer call, or the expert FFN
+DECODE_KERNELS = ("router_logits_gemv", "decode_gate_up", "decode_down_combine")
+FFN_KERNELS = ("ffn_gemv_q4_0", "ffn_mfma")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_traffic.json")
 
 
@@ -57,16 +58,18 @@ def parse():
                    help="write a markdown summary of a --kernel-trace --stats run")
     p.add_argument("--summarize-traffic", nargs=4,
                    metavar=("FETCH_DIR", "WRITE_DIR", "CALIB_MIB", "CMD"),
-                   help="store the expert-FFN HBM traffic per call of --config's workload from "
+                   help="store the HBM traffic per roofline call of --config's workload from "
                         "two --pmc runs (FETCH_SIZE, WRITE_SIZE) made with --copy-calibration")
     return p.parse_args()
 
 
 def ffn_source_digest() -> str:
     h = hashlib.sha256()
-    for f in FFN_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+    d = os.path.join(ROOT, KERNEL_SOURCE_DIR)
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
 
 
@@ -110,7 +113,8 @@ def summarize_traffic(args):
         if copy_kib <= 0:
             sys.exit("no calibration copy found in %s" % d)
         scale = calib / copy_kib
-        ffn = {k: v for k, v in means.items() if "ffn_gemv_q4_0" in k or "ffn_mfma" in k}
+        names = DECODE_KERNELS if decode_path(spec.T, spec.H, spec.I, spec.K) else FFN_KERNELS
+        ffn = {k: v for k, v in means.items() if any(n in k for n in names)}
         out[key + "_bytes"] = sum(ffn.values()) * 1024 * scale
         out[key + "_scale"] = scale
         out[key + "_kib_per_kernel"] = {
@@ -379,6 +383,13 @@ def mfma_path(act: str, T: int, H: int, I: int) -> bool:
     return act == "bf16" and T >= 64 and H % 64 == 0 and I % 64 == 0
 
 
+def decode_path(T: int, H: int, I: int, K: int) -> bool:
+    """Whether the step runs as one moe_layer_decode call: a single token (the
+    call serves up to 8 tokens, but from 2 tokens the four calls are faster),
+    H and I multiples of 64."""
+    return T == 1 and H % 64 == 0 and I % 64 == 0 and K <= 16 and K * (I // 32) * 68 <= 65536
+
+
 def dev_tensor(a, dev="cuda"):
     import numpy as np
     import torch
@@ -431,8 +442,16 @@ def bench_layer(spec, steps: int, warmup: int, nsets: int, cpu_seconds: float = 
         binding.moe_route(xpool[r], s["wr"], bufs.logits, bufs.topk_ids, bufs.topk_w, bufs.offsets,
                           bufs.sorted_slots, bufs.slot_pos, bufs.ws_route, logit_bias=s["bias"])
 
+    # decode batches run as one moe_layer_decode call (router logits, gate/up with
+    # the routing inside, down with the combine inside), others as the four calls
+    fused = decode_path(T, H, I, K)
+
     def step(r, si=None):
         s = sets[r % nsets if si is None else si]
+        if fused:
+            binding.moe_layer_decode(xpool[r], s["wr"], s["gu"], s["dn"], K, expert_scale=s["sc"],
+                                     logit_bias=s["bias"], bufs=bufs)
+            return
         route(r, si)
         binding.moe_expert_ffn_q4_0(xpool[r], s["gu"], s["dn"], K, bufs.offsets,
                                     bufs.sorted_slots, bufs.y_sorted, bufs.ws_ffn)
@@ -460,47 +479,56 @@ def bench_layer(spec, steps: int, warmup: int, nsets: int, cpu_seconds: float = 
     for r in range(warmup):
         step(r % G)
     torch.cuda.synchronize()
+    # S consecutive steps per HIP graph (like consecutive layers of a model in
+    # one graph), so that the timed loop does not measure the host's per-replay
+    # launch cost; graph j holds steps S j .. S j + S - 1
+    S = 8 if T <= 64 and steps % 8 == 0 and G % 8 == 0 else 1
+    NG = G // S
     graphs = []
-    for r in range(G):
+    for j in range(NG):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step(r)
+            for r in range(S * j, S * j + S):
+                step(r)
         graphs.append(g)
     for i in range(warmup):
-        graphs[i % G].replay()
+        graphs[i % NG].replay()
     torch.cuda.synchronize()
-    graphs[0].replay()
-    torch.cuda.synchronize()
-    assert torch.equal(out0, bufs.out), "graph replay differs from eager execution"
-    if nsets > 1 and G > nsets:
-        graphs[nsets].replay()          # batch nsets on set 0, ...
+    # a replay reproduces the eager steps bit for bit (the last step's output)
+    for j in (0, NG - 1):
+        graphs[j].replay()
         torch.cuda.synchronize()
-        out_n = bufs.out.clone()
-        step(nsets)
+        out_g = bufs.out.clone()
+        step(S * j + S - 1)
         torch.cuda.synchronize()
-        assert torch.equal(out_n, bufs.out)
+        assert torch.equal(out_g, bufs.out), "graph replay differs from eager execution"
 
-    # timed region: K steps as graph replays
+    # timed region: K steps as K / S graph replays
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     t_start.record()
-    for i in range(steps):
-        graphs[i % G].replay()
+    for i in range(steps // S):
+        graphs[i % NG].replay()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_step = t_start.elapsed_time(t_end) / steps
 
-    # dominant kernel: the expert-FFN call, with HIP events on its stream around
-    # replays of one graph of F calls (no host launch gap timed)
+    # dominant call, with HIP events on its stream around replays of one graph of
+    # F calls (no host launch gap timed): the decode layer call, or else the
+    # expert-FFN call
     g_ffn = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_ffn):
         for f in range(F):
             s = sets[f]
-            binding.moe_expert_ffn_q4_0(xpool[f], s["gu"], s["dn"], K, routes[f][0], routes[f][1],
-                                        bufs.y_sorted, bufs.ws_ffn)
+            if fused:
+                binding.moe_layer_decode(xpool[f], s["wr"], s["gu"], s["dn"], K,
+                                         expert_scale=s["sc"], logit_bias=s["bias"], bufs=bufs)
+            else:
+                binding.moe_expert_ffn_q4_0(xpool[f], s["gu"], s["dn"], K, routes[f][0],
+                                            routes[f][1], bufs.y_sorted, bufs.ws_ffn)
     g_ffn.replay()
     torch.cuda.synchronize()
     reps = max(2, steps // F)
@@ -525,7 +553,18 @@ def bench_layer(spec, steps: int, warmup: int, nsets: int, cpu_seconds: float = 
     layer_hbm = layer_bytes / (ms_step * 1e-3) / 1e9
     ffn_flops = N * 6.0 * H * I          # per slot 2 (2I H) + 2 (H I)
     layer_tflops = ffn_flops / (ms_step * 1e-3) / 1e12
-    if mfma_path(spec.act, T, H, I):
+    if fused:
+        call_bytes = sum(d * expert_bytes + E * H * 4 + T * H * asz + E * 4 + T * H * 4
+                         for d in distinct[:F]) / F
+        achieved = call_bytes / (ffn_ms * 1e-3) / 1e9
+        roofline = {"kernel": "moe_layer_decode (router logits, gate/up GEMV with top-K and "
+                              "permutation inside, down GEMV with the combine inside: 3 launches)",
+                    "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                    "bytes_per_launch": call_bytes, "avg_launch_us": ffn_ms * 1e3}
+        dtype = ("q4_0 x %s (activation blocks rounded to 15-bit fixed point, exact int4 digit "
+                 "products, fp32 accumulate)" % spec.act)
+    elif mfma_path(spec.act, T, H, I):
         achieved = ffn_flops / (ffn_ms * 1e-3) / 1e12
         roofline = {"kernel": "moe_expert_ffn_q4_0 (activation prep, gate/up and down bf16 MFMA "
                               "grouped GEMM launches)",
@@ -570,9 +609,13 @@ def bench_layer(spec, steps: int, warmup: int, nsets: int, cpu_seconds: float = 
                    "layer_expert_tflops": layer_tflops,
                    "layer_mfma_frac": layer_tflops / BF16_PEAK_TFLOPS,
                    "wall_s": wall,
-                   "timing": "K steps, step i a replay of HIP graph i mod %d (set i mod %d, batch "
-                             "i mod %d); the FFN call over replays of one graph of %d calls on "
-                             "%d sets and routings" % (G, nsets, G, F, F)},
+                   "path": "moe_layer_decode" if fused else "moe_route + moe_expert_ffn_q4_0 + "
+                                                            "moe_combine",
+                   "steps_per_graph": S,
+                   "timing": "K steps as K/%d replays of %d HIP graphs of %d consecutive steps "
+                             "(step i on set i mod %d and batch i mod %d); the roofline call over "
+                             "replays of one graph of %d calls on %d sets and routings"
+                             % (S, NG, S, nsets, G, F, F)},
         "roofline": roofline,
     }
     if cpu_seconds > 0:

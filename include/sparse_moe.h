@@ -181,6 +181,40 @@ moe_status moe_expert_ffn_q4_0(const void* x, int x_dt, int64_t T, int32_t H,
                                size_t ws_bytes, void* stream);
 
 /*
+ * One whole decode layer in one call: the results of moe_route,
+ * moe_expert_ffn_q4_0 and moe_combine, bit for bit, for decode and
+ * verification batches (model card intro: one to eight concurrent requests;
+ * sections "Speed" and "Speculative decoding": decode speed, and drafts of a
+ * few tokens verified in one pass).  Three kernels instead of five: the router
+ * logits; gate/up with top-K and the permutation computed inside every
+ * workgroup (no hand-off through a completion counter); down with the
+ * weighted combine inside (each workgroup owns a few output rows of one token
+ * and sums its K experts there, so no per-slot output y is stored).
+ *
+ *   Arguments are those of the three calls: W_r == NULL selects injected
+ *   logits (then `logits` is an INPUT); logits, topk_ids, topk_w,
+ *   expert_offsets, sorted_slots and slot_pos are OUTPUTS as there (required);
+ *   out_f32 / out_act / residual as in moe_combine (at least one output).
+ *   ws   >= moe_layer_decode_workspace_bytes(T, K, H, I, E, x_dt) bytes (the
+ *        hidden h); contents need no initialisation.
+ * Supported shapes: 1 <= T <= 8, T * K <= 64, H and I multiples of 64, and
+ * K * (I / 32) * 68 bytes of staged hidden digits <= 64 KiB; other shapes
+ * return MOE_ERR_UNSUPPORTED (use the separate calls).  The hidden h goes
+ * through the decode GEMV's 15-bit block fixed point, as in
+ * moe_expert_ffn_q4_0's GEMV path.
+ */
+size_t moe_layer_decode_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_t I, int32_t E,
+                                        int x_dt);
+moe_status moe_layer_decode(const void* x, int x_dt, int64_t T, int32_t H, const float* W_r,
+                            const float* r_scale, const float* logit_bias, int32_t E, int32_t K,
+                            const void* w_gate_up, const void* w_down, int32_t I,
+                            const float* expert_scale, float* logits, int32_t* topk_ids,
+                            float* topk_w, int32_t* expert_offsets, int32_t* sorted_slots,
+                            int32_t* slot_pos, const void* residual, int residual_dt,
+                            float* out_f32, void* out_act, int out_dt, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/*
  * moe_expert_ffn_q4_0 without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, kernels and results as

@@ -38,6 +38,9 @@ SIGNATURES = {
     "moe_expert_ffn_q4_0_workspace_bytes": ([_I64, _I32, _I32, _I32, _I32, C.c_int], _SZ),
     "moe_expert_ffn_q4_0": ([_P, C.c_int, _I64, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P,
                              _SZ, _P], C.c_int),
+    "moe_layer_decode_workspace_bytes": ([_I64, _I32, _I32, _I32, _I32, C.c_int], _SZ),
+    "moe_layer_decode": ([_P, C.c_int, _I64, _I32, _P, _P, _P, _I32, _I32, _P, _P, _I32, _P, _P, _P,
+                          _P, _P, _P, _P, _P, C.c_int, _P, _P, C.c_int, _P, _SZ, _P], C.c_int),
     "moe_expert_ffn_q4_0_noalloc": ([_P, C.c_int, _I64, _I32, _P, _P, _I32, _I32, _I32, _P, _P,
                                      _P, _P], C.c_int),
     "moe_combine": ([_P, _P, _P, _P, _P, _I64, _I32, _I32, _P, C.c_int, _P, _P, C.c_int, _P],
@@ -332,6 +335,52 @@ class LayerBuffers:
         rb = moe_route_workspace_bytes(T, K, E)
         self.ws_route = torch.zeros((max(16, rb),), dtype=torch.uint8, device=device)
         self.ws_ffn = torch.empty((fb,), dtype=torch.uint8, device=device)
+        db = moe_layer_decode_workspace_bytes(T, K, H, I, E, xdt)
+        self.ws_decode = torch.empty((max(16, db),), dtype=torch.uint8, device=device)
+
+
+def moe_layer_decode_workspace_bytes(T: int, K: int, H: int, I: int, E: int, x_dt: int) -> int:
+    return lib.moe_layer_decode_workspace_bytes(T, K, H, I, E, x_dt)
+
+
+def moe_layer_decode(x, W_r, w_gate_up, w_down, K, expert_scale=None, logit_bias=None,
+                     r_scale=None, bufs: Optional[LayerBuffers] = None, logits_in=None,
+                     out_act=None, residual=None, out_f32: bool = True,
+                     stream=None) -> LayerBuffers:
+    """One decode layer (T <= 8 tokens, T*K <= 64) in one call: the routing
+    outputs land in bufs (logits, topk_ids, topk_w, offsets, sorted_slots,
+    slot_pos), the combined output in bufs.out (out_f32) and/or out_act."""
+    T, H = x.shape
+    E = w_gate_up.shape[0]
+    I = w_gate_up.shape[1] // 2
+    if bufs is None:
+        bufs = LayerBuffers(T, H, I, E, K, x.dtype, device=x.device)
+    if logits_in is not None:
+        bufs.logits.copy_(logits_in)
+    wr = None if logits_in is not None else W_r
+    for t, n, d in ((x, "x", None), (wr, "W_r", torch.float32), (w_gate_up, "w_gate_up", torch.uint8),
+                    (w_down, "w_down", torch.uint8), (expert_scale, "expert_scale", torch.float32),
+                    (r_scale, "r_scale", torch.float32), (logit_bias, "logit_bias", torch.float32),
+                    (out_act, "out_act", None), (residual, "residual", None)):
+        _dev(t, n, d)
+    if w_gate_up.numel() != E * 2 * I * (H // 32) * 18 or w_down.numel() != E * H * (I // 32) * 18:
+        raise ValueError("Q4_0 weight sizes disagree with [E][2I][H/32][18] / [E][H][I/32][18]")
+    if wr is not None and tuple(wr.shape) != (E, H):
+        raise ValueError("W_r must be [E, H]")
+    if tuple(bufs.logits.shape) != (T, E) or tuple(bufs.topk_ids.shape) != (T, K):
+        raise ValueError("layer buffers do not match the call")
+    rdt = act_dtype(residual) if residual is not None else MOE_F32
+    odt = act_dtype(out_act) if out_act is not None else MOE_F32
+    _check(lib.moe_layer_decode(_ptr(x), act_dtype(x), T, H, _ptr(wr), _ptr(r_scale),
+                                _ptr(logit_bias), E, K, _ptr(w_gate_up), _ptr(w_down), I,
+                                _ptr(expert_scale), _ptr(bufs.logits), _ptr(bufs.topk_ids),
+                                _ptr(bufs.topk_w), _ptr(bufs.offsets), _ptr(bufs.sorted_slots),
+                                _ptr(bufs.slot_pos), _ptr(residual), rdt,
+                                _ptr(bufs.out) if out_f32 else None, _ptr(out_act), odt,
+                                _ptr(bufs.ws_decode),
+                                bufs.ws_decode.numel() * bufs.ws_decode.element_size(),
+                                _stream(stream)), "moe_layer_decode")
+    return bufs
 
 
 def moe_layer(x, W_r, w_gate_up, w_down, K, expert_scale=None, logit_bias=None, r_scale=None,

@@ -207,6 +207,54 @@ moe_status moe_expert_ffn_q4_0(const void* x, int x_dt, int64_t T, int32_t H,
                                            (hipStream_t)stream));
 }
 
+size_t moe_layer_decode_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_t I, int32_t E,
+                                        int x_dt) {
+    if (check_ekh(T, K, E) != MOE_OK || check_dim(H, MOE_MAX_H) != MOE_OK ||
+        check_dim(I, MOE_MAX_I) != MOE_OK || !dtype_ok(x_dt))
+        return 0;
+    // the hidden h [T*K, I] in the activation dtype, in sorted-slot order
+    return round_up((size_t)(T * K) * (size_t)I * (x_dt == MOE_F32 ? 4 : 2), 256);
+}
+
+moe_status moe_layer_decode(const void* x, int x_dt, int64_t T, int32_t H, const float* W_r,
+                            const float* r_scale, const float* logit_bias, int32_t E, int32_t K,
+                            const void* w_gate_up, const void* w_down, int32_t I,
+                            const float* expert_scale, float* logits, int32_t* topk_ids,
+                            float* topk_w, int32_t* expert_offsets, int32_t* sorted_slots,
+                            int32_t* slot_pos, const void* residual, int residual_dt,
+                            float* out_f32, void* out_act, int out_dt, void* ws, size_t ws_bytes,
+                            void* stream) {
+    moe_status s = check_ekh(T, K, E);
+    if (s != MOE_OK) return s;
+    if ((s = check_dim(H, MOE_MAX_H)) != MOE_OK || (s = check_dim(I, MOE_MAX_I)) != MOE_OK) return s;
+    if (!dtype_ok(x_dt) || !dtype_ok(out_dt) || (residual && !dtype_ok(residual_dt)))
+        return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!moe::decode_layer_supported(T, H, I, K)) return MOE_ERR_UNSUPPORTED;
+    if (!x || !logits || !topk_ids || !topk_w || !expert_offsets || !sorted_slots || !slot_pos ||
+        !w_gate_up || !w_down || (!out_f32 && !out_act))
+        return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w) ||
+        !aligned16(expert_offsets) || !aligned16(sorted_slots) || !aligned16(slot_pos) ||
+        !aligned16(w_gate_up) || !aligned16(w_down) ||
+        (W_r && (!aligned16(W_r) || (r_scale && !aligned16(r_scale)) ||
+                 (logit_bias && !aligned16(logit_bias)))) ||
+        (expert_scale && !aligned16(expert_scale)) || (residual && !aligned16(residual)) ||
+        (out_f32 && !aligned16(out_f32)) || (out_act && !aligned16(out_act)))
+        return MOE_ERR_ALIGN;
+    const size_t need = moe_layer_decode_workspace_bytes(T, K, H, I, E, x_dt);
+    if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOE_ERR_ALIGN;
+    hipStream_t st = (hipStream_t)stream;
+    if (W_r && (s = hip_status(moe::launch_router_logits(x, x_dt, T, H, W_r, r_scale, logit_bias, E,
+                                                        logits, st))) != MOE_OK)
+        return s;
+    return hip_status(moe::launch_decode_layer(
+        x, x_dt, (int)T, H, logits, E, K, (const uint8_t*)w_gate_up, (const uint8_t*)w_down, I,
+        expert_scale, topk_ids, topk_w, expert_offsets, sorted_slots, slot_pos, residual,
+        residual_dt, out_f32, out_act, out_dt, ws, st));
+}
+
 moe_status moe_expert_ffn_q4_0_noalloc(const void* x, int x_dt, int64_t T, int32_t H,
                                        const void* w_gate_up, const void* w_down, int32_t I,
                                        int32_t E, int32_t K, const int32_t* expert_offsets,

@@ -27,7 +27,7 @@
 // wave are contiguous.
 #include <type_traits>
 
-#include "kernels.h"
+#include "route_dev.h"
 
 namespace moe {
 
@@ -229,11 +229,29 @@ constexpr int steps_per_wave() {
 // trade when the grid is several times the chip (many experts, few tokens).
 // ONE: a single-token call, so every gate/up slot reads activation row 0 (no
 // dependent read of the slot's token before the activation loads).
-template <int MODE, int ADT, int LPR, int TC, int UPW, bool EVEN_NB, bool DIRECT, bool ONE>
+// One lane's share of a row's dot product: its block pair's exact integer
+// products with the activation digits, scaled by d * (max|v| / 30583) per block.
+MOE_DEV float pair_acc(const PairDec& w, const uint32_t* xa, const uint32_t* xb, float sa, float sb) {
+    const int ia = block_idot(w.qA, xa);
+    const int ib = block_idot(w.qB, xb);
+    return fmaf(w.dA * sa, (float)ia, (w.dB * sb) * (float)ib);
+}
+
+// Routing prologue of gemv_tile that does nothing (the routing is an input, and
+// the workgroup's expert is looked up from the offsets).  A prologue that
+// routes the batch itself returns true when it also knows the workgroup's
+// expert e, its first sorted slot p0 and slot count n.
+struct NoRoute {
+    __device__ __forceinline__ bool operator()(int, int&, int&, int&) const { return false; }
+};
+
+template <int MODE, int ADT, int LPR, int TC, int UPW, bool EVEN_NB, bool DIRECT, bool ONE,
+          bool SLOT_H = false, class Route = NoRoute>
 MOE_DEV void gemv_tile(const uint8_t* __restrict__ W, int nb, int I, int H,
-                       const void* __restrict__ act, const int32_t* __restrict__ offsets,
-                       const int32_t* __restrict__ sorted_slots, int K, int E,
-                       void* __restrict__ out, int wave_lds_bytes, uint8_t* smem, int bx, int by) {
+                       const void* __restrict__ act, const int32_t* offsets,
+                       const int32_t* sorted_slots, int K, int E,
+                       void* __restrict__ out, int wave_lds_bytes, uint8_t* smem, int bx, int by,
+                       Route route = Route()) {
     constexpr int RPS = 64 / LPR;
     constexpr int RPW = RPS * UPW;           // rows (MODE 0: row pairs) per wave
     constexpr int NR = (MODE == 0) ? 2 : 1;  // spans per wave (gate, up)
@@ -242,48 +260,14 @@ MOE_DEV void gemv_tile(const uint8_t* __restrict__ W, int nb, int I, int H,
     __shared__ int s_e, s_p0, s_n, s_wcnt[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    // -- which expert: the by-th expert with at least one slot
-    {
-        const int e = tid;
-        int o0 = 0, o1 = 0;
-        if (e < E) {
-            o0 = offsets[e];
-            o1 = offsets[e + 1];
-        }
-        const bool ne = o1 > o0;
-        const uint64_t b = __ballot(ne);
-        if (tid == 0) s_e = -1;
-        if (lane == 0) s_wcnt[wave] = __popcll(b);
-        __syncthreads();
-        int before = __popcll(b & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-        for (int w = 0; w < wave; ++w) before += s_wcnt[w];
-        if (ne && before == by) {
-            s_e = e;
-            s_p0 = o0;
-            s_n = o1 - o0;
-        }
-        __syncthreads();
-    }
-    const int e = s_e;
-    if (e < 0) return;
-    const int p0 = s_p0, ne_tok = s_n;
-
-    const int rows_out = (MODE == 0) ? I : H;            // outputs per expert
-    const int rows_tot = (MODE == 0) ? 2 * I : H;        // stored rows per expert
-    const int64_t row_bytes = (int64_t)nb * 18;
-    const uint8_t* We = W + (int64_t)e * rows_tot * row_bytes;
-    const int g = lane / LPR, q = lane % LPR;
-    const int nblk_here = min(2, max(0, nb - 2 * q));
-    const int row0 = (bx * 4 + wave) * RPW;              // first output row of this wave
-    const int nrows = max(0, min(RPW, rows_out - row0));
-
-    uint8_t* wl = smem + wave * wave_lds_bytes;
-    const int span_bytes = NCH * 1024 - 16;
     const int nbp = (nb + 1) & ~1;  // blocks per activation row, rounded up to a pair
     uint32_t* dig = reinterpret_cast<uint32_t*>(smem + 4 * wave_lds_bytes);
     float* dsc = reinterpret_cast<float*>(dig + TC * 16 * nbp);
     const int in_len = (MODE == 0) ? H : I;
     constexpr int NTASK = 2 * TC;  // quarter-block tasks per thread: TC * 128 blocks * 4 / 256
+    // this workgroup's expert: first slot and slot count (set by the lookup below;
+    // a single-token call has one slot per expert)
+    int p0 = 0, ne_tok = 1;
 
     // activation rows of a chunk -> registers (one quarter block per task)
     float xv[NTASK][8];
@@ -328,7 +312,53 @@ MOE_DEV void gemv_tile(const uint8_t* __restrict__ W, int nb, int I, int H,
         }
     };
 
-    load_x(0);  // first: so that waiting for the activations does not wait for the weights
+    // the activations first, so that waiting for them does not wait for the
+    // weights; the gate/up product of a single-token call reads row 0 of x
+    // whatever the routing, so it issues them before the routing is known
+    constexpr bool EARLY_X = ONE && MODE == 0;
+    if constexpr (EARLY_X) load_x(0);
+    // the routing prologue (a fused decode layer) or nothing
+    int e = -1;
+    if (!route(by, e, p0, ne_tok)) {
+        // which expert: the by-th expert with at least one slot
+        const int ex = tid;
+        int o0 = 0, o1 = 0;
+        if (ex < E) {
+            o0 = offsets[ex];
+            o1 = offsets[ex + 1];
+        }
+        const bool ne = o1 > o0;
+        const uint64_t b = __ballot(ne);
+        if (tid == 0) s_e = -1;
+        if (lane == 0) s_wcnt[wave] = __popcll(b);
+        __syncthreads();
+        int before = __popcll(b & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+        for (int w = 0; w < wave; ++w) before += s_wcnt[w];
+        if (ne && before == by) {
+            s_e = ex;
+            s_p0 = o0;
+            s_n = o1 - o0;
+        }
+        __syncthreads();
+        e = s_e;
+        if (e < 0) return;
+        p0 = s_p0;
+        ne_tok = s_n;
+    }
+
+    if constexpr (!EARLY_X) load_x(0);
+
+    const int rows_out = (MODE == 0) ? I : H;            // outputs per expert
+    const int rows_tot = (MODE == 0) ? 2 * I : H;        // stored rows per expert
+    const int64_t row_bytes = (int64_t)nb * 18;
+    const uint8_t* We = W + (int64_t)e * rows_tot * row_bytes;
+    const int g = lane / LPR, q = lane % LPR;
+    const int nblk_here = min(2, max(0, nb - 2 * q));
+    const int row0 = (bx * 4 + wave) * RPW;              // first output row of this wave
+    const int nrows = max(0, min(RPW, rows_out - row0));
+
+    uint8_t* wl = smem + wave * wave_lds_bytes;
+    const int span_bytes = NCH * 1024 - 16;
 
     // -- this wave's rows: all loads in flight at once (into registers)
     constexpr int NCHS = DIRECT ? 1 : NCH;
@@ -406,11 +436,7 @@ MOE_DEV void gemv_tile(const uint8_t* __restrict__ W, int nb, int I, int H,
                     w = lds_pair<EVEN_NB>(wl + r * (span_bytes + 16) + (nh > 0 ? off : 0), nh);
                 }
 #pragma unroll
-                for (int t = 0; t < TC; ++t) {
-                    const int ia = block_idot(w.qA, xa[t]);
-                    const int ib = block_idot(w.qB, xb[t]);
-                    acc[r][t] = fmaf(w.dA * sa[t], (float)ia, (w.dB * sb[t]) * (float)ib);
-                }
+                for (int t = 0; t < TC; ++t) acc[r][t] = pair_acc(w, xa[t], xb[t], sa[t], sb[t]);
             }
 #pragma unroll
             for (int t = 0; t < TC; ++t)
@@ -438,7 +464,8 @@ MOE_DEV void gemv_tile(const uint8_t* __restrict__ W, int nb, int I, int H,
                 const int64_t p = p0 + c0 + t;
                 const int row = row0 + u;
                 if (MODE == 0)
-                    store_act(out, ADT, p * I + row, gelu_tanh(mine[0]) * mine[NR - 1]);
+                    store_act(out, ADT, (SLOT_H ? (int64_t)sorted_slots[p] : p) * I + row,
+                              gelu_tanh(mine[0]) * mine[NR - 1]);
                 else
                     reinterpret_cast<float*>(out)[p * H + row] = mine[0];
             }
@@ -452,7 +479,8 @@ MOE_DEV void gemv_tile(const uint8_t* __restrict__ W, int nb, int I, int H,
                         const int64_t p = p0 + c0 + t;
                         const int row = row0 + lr;
                         if (MODE == 0)
-                            store_act(out, ADT, p * I + row, gelu_tanh(res[u][t][0]) * res[u][t][NR - 1]);
+                            store_act(out, ADT, (SLOT_H ? (int64_t)sorted_slots[p] : p) * I + row,
+                                      gelu_tanh(res[u][t][0]) * res[u][t][NR - 1]);
                         else
                             reinterpret_cast<float*>(out)[p * H + row] = res[u][t][0];
                     }
@@ -560,6 +588,293 @@ hipError_t launch_ffn_gemv(const void* x, int x_dt, int64_t T, int H, const uint
         f32 ? go(F32{}, One{}, Direct{}, Many{}) : go(BF16{}, One{}, Direct{}, Many{});
     else
         f32 ? go(F32{}, Two{}, Direct{}, Many{}) : go(BF16{}, Two{}, Direct{}, Many{});
+    return hipGetLastError();
+}
+
+// ---- one decode layer in three launches ---------------------------------------------
+// Router logits (the few-token router kernel), then gate/up with the routing
+// inside, then down with the combine inside.  Each step is computed with the
+// same per-token arithmetic as the four-call path (routing kernels, GEMV,
+// combine), so every output is the same bit for bit; what changes is that
+// top-K and the permutation run in every gate/up workgroup (no last-workgroup
+// hand-off through global memory) and that no per-slot expert output y is
+// stored and read back.
+
+// Routing of a decode batch (T <= 8 tokens, T * K <= 64 slots) by one
+// workgroup from the router logits: one token by wave 0 (route_one_token);
+// more tokens: top-K of every token (wave w takes tokens w and w + 4), then
+// the permutation of the slots by wave 0.
+struct DecodeRouting {
+    int32_t ids[PERM_WAVE];
+    float w[PERM_WAVE];
+    int32_t off[MOE_MAX_E + 1];
+    int32_t ss[PERM_WAVE], sp[PERM_WAVE];
+};
+
+MOE_DEV void decode_route(const float* __restrict__ logits, int T, int E, int K, DecodeRouting& R) {
+    if (T == 1) {  // one token: one wave, short dependency chains
+        if (threadIdx.x < 64) route_one_token<false>(logits, E, K, R.ids, R.w, R.off, R.ss, R.sp);
+        __syncthreads();
+        return;
+    }
+    const int wave = threadIdx.x >> 6;
+    const int t0 = wave, t1 = wave + 4;
+    if (t1 < T) {
+        float v[2][4];
+        topk_load(logits + (int64_t)t0 * E, E, v[0]);
+        topk_load(logits + (int64_t)t1 * E, E, v[1]);
+        int32_t* const ip[2] = {R.ids + t0 * K, R.ids + t1 * K};
+        float* const wp[2] = {R.w + t0 * K, R.w + t1 * K};
+        topk_select_n<2>(v, E, K, ip, wp);
+    } else if (t0 < T) {
+        float v[4];
+        topk_load(logits + (int64_t)t0 * E, E, v);
+        topk_select(v, E, K, R.ids + t0 * K, R.w + t0 * K);
+    }
+    __syncthreads();
+    if (wave == 0) permute_wave(R.ids, T * K, E, R.off, R.ss, R.sp);
+    __syncthreads();
+}
+
+// Gate/up of a decode layer: every workgroup routes the batch itself (into
+// LDS), then computes its tile of the by-th active expert as the expert FFN's
+// gate/up kernel does, storing the hidden h by slot (token-major) instead of
+// by sorted position.  Workgroup (0, 0) also stores the routing.
+template <int ADT, int LPR, int TC, int UPW, bool DIRECT, bool ONE>
+__global__ __launch_bounds__(256) void decode_gate_up(
+    const uint8_t* __restrict__ W, int nb, int I, int H, const void* __restrict__ x,
+    const float* __restrict__ logits, int T, int E, int K, int32_t* __restrict__ ids_out,
+    float* __restrict__ w_out, int32_t* __restrict__ off_out, int32_t* __restrict__ ss_out,
+    int32_t* __restrict__ sp_out, void* __restrict__ h_out, int wave_lds_bytes) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ DecodeRouting R;
+    auto route = [&](int by, int& e, int& p0, int& n) {
+        decode_route(logits, T, E, K, R);
+        if (blockIdx.x == 0 && blockIdx.y == 0) {
+            const int tid = threadIdx.x;
+            if (tid < T * K) {
+                ids_out[tid] = R.ids[tid];
+                w_out[tid] = R.w[tid];
+                ss_out[tid] = R.ss[tid];
+                sp_out[tid] = R.sp[tid];
+            }
+            for (int x = tid; x <= E; x += 256) off_out[x] = R.off[x];
+        }
+        if (T != 1) return false;
+        // one token: K distinct experts, one slot each, the by-th in sorted order
+        p0 = by;
+        n = 1;
+        e = R.ids[R.ss[by]];
+        return true;
+    };
+    gemv_tile<0, ADT, LPR, TC, UPW, true, DIRECT, ONE, true>(W, nb, I, H, x, R.off, R.ss, K, E,
+                                                             h_out, wave_lds_bytes, smem, blockIdx.x,
+                                                             blockIdx.y, route);
+}
+
+// Down and combine of a decode layer.  Workgroup (bx, t): output rows
+// RR * bx .. + RR - 1 of token t.  It digitises the hidden rows of
+// the token's K slots, computes those output rows of its K experts with the
+// down GEMV's lane layout and arithmetic (a unit = one expert's row, LPR lanes,
+// each lane a block pair in registers), and sums them in the combine's fixed
+// k order with the routing weight times the expert scale, adding the
+// residual for the activation-type output.
+template <int ADT, int LPR, int KB, int RR>
+__global__ __launch_bounds__(256) void decode_down_combine(
+    const uint8_t* __restrict__ Wd, int nb, int H, const void* __restrict__ hbuf,
+    const int32_t* __restrict__ ids, const float* __restrict__ tw,
+    const float* __restrict__ scale, int K,
+    const void* __restrict__ residual, int rdt, float* __restrict__ out_f32,
+    void* __restrict__ out_act, int odt) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr int RPS = 64 / LPR;                               // units per wave step
+    constexpr int UPW = (KB * RR + 4 * RPS - 1) / (4 * RPS);  // steps per wave
+    constexpr int NTB = 4;                                      // hidden quarter blocks per thread and round
+    __shared__ float ys[KB][RR];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane / LPR, q = lane % LPR;
+    const int t = blockIdx.y, r0 = blockIdx.x * RR;
+    const int I = nb * 32;
+    const int64_t row_bytes = (int64_t)nb * 18;
+    uint32_t* dig = reinterpret_cast<uint32_t*>(smem);  // [K][16][nb] digit words
+    float* dsc = reinterpret_cast<float*>(dig + K * 16 * nb);  // [K][nb] block scales
+
+    // a lane's slot k of the token (k clamped below K): its expert, each lane
+    // loading that of its own k (a few distinct addresses per wave); the hidden
+    // rows are stored by slot, t * K + k, so their loads need no routing
+    const int32_t* ids_t = ids + (int64_t)t * K;
+    // hidden rows -> registers, one quarter block per task (unconditional,
+    // clamped loads so that their number is static)
+    const int ntask = K * nb * 4;
+    float xv[NTB][8];
+    auto load_h = [&](int round) {
+#pragma unroll
+        for (int i = 0; i < NTB; ++i) {
+            const int task = tid + 256 * (NTB * round + i);
+            const bool ok = task < ntask;
+            const int m = task & 3, tb = task >> 2, k = tb / nb, b = tb % nb;
+            const int64_t s = (int64_t)t * K + (ok ? k : 0);
+            load_quarter<ADT>(hbuf, s * I + b * 32, m, xv[i]);
+        }
+    };
+    auto digitize_h = [&](int round) {
+#pragma unroll
+        for (int i = 0; i < NTB; ++i) {
+            const int task = tid + 256 * (NTB * round + i);
+            if (task < ntask) {
+                const int m = task & 3, tb = task >> 2, k = tb / nb, b = tb % nb;
+                digitize_quarter(xv[i], m, dig + k * 16 * nb + b, nb, dsc + k * nb + b);
+            }
+        }
+    };
+    load_h(0);
+    // this lane's weight windows: unit u = (wave * UPW + s) * RPS + g is row
+    // u % RR of slot u / RR (units past the K slots load slot K-1's)
+    const int qq = min(q, nb / 2 - 1);
+    uint32_t wd[UPW][9];
+#pragma unroll
+    for (int s = 0; s < UPW; ++s) {
+        const int u = (wave * UPW + s) * RPS + g;
+        const int k = min(u / RR, K - 1), r = u % RR;
+        const uint8_t* pw = Wd + ((int64_t)ids_t[k] * H + r0 + r) * row_bytes + 36 * qq;
+        const u32x4a4 a = *reinterpret_cast<const u32x4a4*>(pw);
+        const u32x4a4 b = *reinterpret_cast<const u32x4a4*>(pw + 16);
+        const uint32_t c = *reinterpret_cast<const uint32_t*>(pw + 32);
+        wd[s][0] = a.x; wd[s][1] = a.y; wd[s][2] = a.z; wd[s][3] = a.w;
+        wd[s][4] = b.x; wd[s][5] = b.y; wd[s][6] = b.z; wd[s][7] = b.w;
+        wd[s][8] = c;
+    }
+    // combine factors (used last)
+    float ck[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+        const int64_t s = (int64_t)t * K + min(k, K - 1);
+        ck[k] = tw[s] * (scale ? scale[ids[s]] : 1.f);
+    }
+    digitize_h(0);
+    const int rounds = (ntask + 256 * NTB - 1) / (256 * NTB);
+    for (int round = 1; round < rounds; ++round) {
+        load_h(round);
+        digitize_h(round);
+    }
+    __syncthreads();  // the digits of all K slots are in LDS
+    const int nblk_here = min(2, max(0, nb - 2 * q));
+    const int qp = min(q, nb / 2 - 1);
+#pragma unroll
+    for (int s = 0; s < UPW; ++s) {
+        const int u = (wave * UPW + s) * RPS + g;
+        const int k = u / RR, r = u % RR;
+        const bool valid = k < K;
+        const int kk = min(k, K - 1);
+        const PairDec w = reg_pair(wd[s], valid ? nblk_here : 0);
+        uint32_t xa[16], xb[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint2 v = reinterpret_cast<const uint2*>(dig + (kk * 16 + i) * nb)[qp];
+            xa[i] = v.x;
+            xb[i] = v.y;
+        }
+        const float2 sv = reinterpret_cast<const float2*>(dsc + kk * nb)[qp];
+        const float y = group_sum<LPR>(pair_acc(w, xa, xb, sv.x, sv.y));
+        if (valid && q == LPR - 1) ys[k][r] = y;
+    }
+    __syncthreads();
+    if (tid < RR) {
+        float acc = 0.f;
+#pragma unroll
+        for (int k = 0; k < KB; ++k)
+            if (k < K) acc = fmaf(ck[k], ys[k][tid], acc);
+        const int64_t o = (int64_t)t * H + r0 + tid;
+        if (out_f32) out_f32[o] = acc;
+        if (out_act) store_act(out_act, odt, o, residual ? acc + load_act(residual, rdt, o) : acc);
+    }
+}
+
+// output rows per workgroup of the fused down + combine (a divisor of 64)
+constexpr int DECODE_DOWN_ROWS = 16;
+
+size_t decode_down_lds_bytes(int K, int I) { return (size_t)K * (I / 32) * 17 * sizeof(uint32_t); }
+
+bool decode_layer_supported(int64_t T, int H, int I, int K) {
+    return T >= 1 && T <= ROUTER_GEMV_MAX_T && T * K <= PERM_WAVE && H % 64 == 0 && I % 64 == 0 &&
+           decode_down_lds_bytes(K, I) <= 64 * 1024;
+}
+
+template <int ADT, int LPR, int TC, bool DIRECT, bool ONE>
+static void launch_decode_gate_up(const uint8_t* W, int nb, int I, int H, const void* x,
+                                  const float* logits, int T, int E, int K, int n_active,
+                                  int32_t* ids, float* w, int32_t* off, int32_t* ss, int32_t* sp,
+                                  void* h, hipStream_t st) {
+    constexpr int RPS = 64 / LPR;
+    constexpr int UPW = steps_per_wave<0, LPR, DIRECT>();
+    constexpr int RPW = RPS * UPW;
+    const int wgs = (I + 4 * RPW - 1) / (4 * RPW);
+    constexpr int NCH = (RPW * 36 * LPR + 15 + 1023) / 1024;
+    const int wave_lds = DIRECT ? 0 : 2 * NCH * 1024;
+    const size_t lds = (size_t)4 * wave_lds + (size_t)TC * nb * 17 * sizeof(uint32_t);
+    decode_gate_up<ADT, LPR, TC, UPW, DIRECT, ONE><<<dim3(wgs, n_active), 256, lds, st>>>(
+        W, nb, I, H, x, logits, T, E, K, ids, w, off, ss, sp, h, wave_lds);
+}
+
+hipError_t launch_decode_layer(const void* x, int x_dt, int T, int H, const float* logits, int E,
+                               int K, const uint8_t* w_gate_up, const uint8_t* w_down, int I,
+                               const float* scale, int32_t* ids, float* w, int32_t* off,
+                               int32_t* ss, int32_t* sp, const void* residual, int rdt,
+                               float* out_f32, void* out_act, int odt, void* h_ws,
+                               hipStream_t st) {
+    const int N = T * K, n_active = min(E, N);
+    // gate/up: the expert FFN's choice of chunk size and load path
+    auto gu = [&](auto adt, auto tc, auto direct, auto one) {
+        constexpr int A = decltype(adt)::value, TC = decltype(tc)::value;
+        constexpr bool D = decltype(direct)::value, O = decltype(one)::value;
+        const int nb = H / 32, pairs = nb / 2;
+#define MOE_DGU_CASE(L)                                                                        \
+        if (pairs <= L) {                                                                      \
+            launch_decode_gate_up<A, L, TC, D, O>(w_gate_up, nb, I, H, x, logits, T, E, K,     \
+                                                  n_active, ids, w, off, ss, sp, h_ws, st);    \
+            return;                                                                            \
+        }
+        MOE_DGU_CASE(1) MOE_DGU_CASE(2) MOE_DGU_CASE(4) MOE_DGU_CASE(8) MOE_DGU_CASE(16)
+        MOE_DGU_CASE(32) MOE_DGU_CASE(64)
+#undef MOE_DGU_CASE
+    };
+    using F32 = std::integral_constant<int, MOE_F32>;
+    using BF16 = std::integral_constant<int, MOE_BF16>;
+    using One = std::integral_constant<int, 1>;
+    using Two = std::integral_constant<int, 2>;
+    const bool f32 = x_dt == MOE_F32;
+    if (T == 1)
+        f32 ? gu(F32{}, One{}, std::false_type{}, std::true_type{})
+            : gu(BF16{}, One{}, std::false_type{}, std::true_type{});
+    else if (N <= E)
+        f32 ? gu(F32{}, One{}, std::true_type{}, std::false_type{})
+            : gu(BF16{}, One{}, std::true_type{}, std::false_type{});
+    else
+        f32 ? gu(F32{}, Two{}, std::true_type{}, std::false_type{})
+            : gu(BF16{}, Two{}, std::true_type{}, std::false_type{});
+    // down + combine
+    const int nb = I / 32, pairs = nb / 2;
+    const size_t lds = decode_down_lds_bytes(K, I);
+    constexpr int RR = DECODE_DOWN_ROWS;
+    const dim3 grid(H / RR, T);
+    auto dc = [&](auto adt, auto kb) {
+        constexpr int A = decltype(adt)::value, KB = decltype(kb)::value;
+#define MOE_DDC_CASE(L)                                                                          \
+        if (pairs <= L) {                                                                        \
+            decode_down_combine<A, L, KB, RR><<<grid, 256, lds, st>>>(                           \
+                w_down, nb, H, h_ws, ids, w, scale, K, residual, rdt, out_f32, out_act, odt);     \
+            return;                                                                              \
+        }
+        MOE_DDC_CASE(1) MOE_DDC_CASE(2) MOE_DDC_CASE(4) MOE_DDC_CASE(8) MOE_DDC_CASE(16)
+        MOE_DDC_CASE(32) MOE_DDC_CASE(64)
+#undef MOE_DDC_CASE
+    };
+    using K8 = std::integral_constant<int, 8>;
+    using K16 = std::integral_constant<int, 16>;
+    if (K <= 8)
+        f32 ? dc(F32{}, K8{}) : dc(BF16{}, K8{});
+    else
+        f32 ? dc(F32{}, K16{}) : dc(BF16{}, K16{});
     return hipGetLastError();
 }
 

@@ -30,6 +30,17 @@ hipError_t launch_ffn_gemv(const void* x, int x_dt, int64_t T, int H, const uint
                            const int32_t* offsets, const int32_t* sorted_slots, void* h_ws,
                            float* y_sorted, hipStream_t st);
 
+// one decode layer (router logits, gate/up with the routing inside, down with
+// the combine inside): up to ROUTER_GEMV_MAX_T tokens and 64 slots, rows of an
+// even number of Q4_0 blocks
+bool decode_layer_supported(int64_t T, int H, int I, int K);
+hipError_t launch_decode_layer(const void* x, int x_dt, int T, int H, const float* logits, int E,
+                               int K, const uint8_t* w_gate_up, const uint8_t* w_down, int I,
+                               const float* scale, int32_t* ids, float* w, int32_t* off,
+                               int32_t* ss, int32_t* sp, const void* residual, int rdt,
+                               float* out_f32, void* out_act, int odt, void* h_ws,
+                               hipStream_t st);
+
 // bf16 activations, enough tokens, and rows of an even number of Q4_0 blocks
 // (every block pair dword aligned)
 inline bool ffn_use_mfma(int x_dt, int64_t T, int H, int I) {

@@ -280,6 +280,89 @@ MOE_DEV void topk_select_n(const float (&lv)[NT][4], int E, int K, int32_t* cons
     }
 }
 
+// Routing of ONE token by one wave, for latency: the same K rounds of a wave
+// arg-max as topk_select (the largest key by DPP reductions; the lowest expert
+// holding it by ballots, as a first set bit, instead of a second reduction),
+// recording the round in which each expert is taken; then the permutation of
+// the token's K slots from the set of kept experts: expert e's offset is the
+// number of kept experts below e (a masked bit count), which is also the sorted
+// position of the slot that took it.  Same ids, weights and permutation as
+// topk_select and permute_wave, bit for bit.  ids, w, offsets, sorted_slots
+// and slot_pos may point to LDS or global memory.  Every lane of the wave must
+// be active.  COH: the logits were written by other workgroups of this launch.
+template <bool COH>
+MOE_DEV void route_one_token(const float* logits, int E, int K, int32_t* ids, float* w,
+                             int32_t* offsets, int32_t* sorted_slots, int32_t* slot_pos) {
+    const int lane = threadIdx.x & 63;
+    float v[4];
+    topk_load<COH>(logits, E, v);
+    int key[4], rk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        key[i] = lane + 64 * i < E ? topk_key(v[i] + 0.f) : INT_MIN;
+        rk[i] = -1;
+    }
+    float selv[MOE_MAX_K];
+    int seli[MOE_MAX_K];
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_K; ++k) {
+        selv[k] = 0.f;
+        seli[k] = 0;
+        if (k < K) {
+            const int m = wave_max_i32(max(max(key[0], key[1]), max(key[2], key[3])));
+            // the lowest expert holding m: experts 64 i + lane, so the first key
+            // register with a match, then its first lane
+            uint64_t b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) b[i] = __ballot(key[i] == m);
+            const int idx = b[0] ? __builtin_ctzll(b[0])
+                          : b[1] ? 64 + __builtin_ctzll(b[1])
+                          : b[2] ? 128 + __builtin_ctzll(b[2])
+                                 : 192 + __builtin_ctzll(b[3]);
+            selv[k] = topk_unkey(m);
+            seli[k] = idx;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool taken = 64 * i + lane == idx;
+                key[i] = taken ? INT_MIN : key[i];
+                rk[i] = taken ? k : rk[i];
+            }
+        }
+    }
+    // softmax over the K kept logits (topk_select_n's arithmetic)
+    float myv = 0.f;
+    int myi = 0;
+#pragma unroll
+    for (int k = 0; k < MOE_MAX_K; ++k)
+        if (k == lane) {
+            myv = selv[k];
+            myi = seli[k];
+        }
+    const float ex = lane < K ? expf(myv - selv[0]) : 0.f;
+    const float s = group_sum<16>(ex);
+    if (lane < K) {
+        ids[lane] = myi;
+        w[lane] = ex / s;
+    }
+    // permutation: slot k (taken in round k) of expert e sits at offsets[e]
+    int below = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint64_t kept = __ballot(rk[i] >= 0);
+        const int off = below + (int)__builtin_amdgcn_mbcnt_hi(
+                                    (uint32_t)(kept >> 32),
+                                    __builtin_amdgcn_mbcnt_lo((uint32_t)kept, 0u));
+        const int e = lane + 64 * i;
+        if (e < E) offsets[e] = off;
+        if (rk[i] >= 0) {
+            sorted_slots[off] = rk[i];
+            slot_pos[rk[i]] = off;
+        }
+        below += __popcll(kept);
+    }
+    if (lane == 0) offsets[E] = below;
+}
+
 MOE_DEV void topk_select(const float (&lv)[4], int E, int K, int32_t* ids, float* w) {
     const float (&l1)[1][4] = *reinterpret_cast<const float (*)[1][4]>(&lv);
     int32_t* const i1[1] = {ids};

@@ -233,6 +233,11 @@ __global__ __launch_bounds__(256) void route_small(const void* __restrict__ x, i
     }
     __syncthreads();
     if (!s_last) return;
+    if (T == 1) {  // one token: one wave, short dependency chains
+        if (wave == 0) route_one_token<true>(logits, E, K, ids, w, offsets, sorted_slots, slot_pos);
+        if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
     // wave w takes tokens w and w + 4 (both selections interleaved)
     const int t0 = wave, t1 = wave + 4;
     if (t1 < T) {

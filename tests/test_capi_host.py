@@ -121,6 +121,34 @@ def test_ffn_noalloc_validation():
     assert big(934, 8, 2816, 704, 128, 1) <= 16 << 20 < big(935, 8, 2816, 704, 128, 1)
 
 
+def test_decode_layer_validation_and_workspace():
+    f = lib.moe_layer_decode
+    ws = lib.moe_layer_decode_workspace_bytes(1, 8, 2816, 704, 128, 0)
+    assert ws >= 8 * 704 * 4 and ws % 256 == 0
+    assert lib.moe_layer_decode_workspace_bytes(1, 8, 2800, 704, 128, 0) == 0   # H % 32
+    UNS = 4
+
+    def call(x=A, xdt=0, T=1, H=2816, wr=A, E=128, K=8, I=704, ws_=A, wsb=ws, out=A, act=None,
+             odt=0, logits=A):
+        # (x, x_dt, T, H, W_r, r_scale, bias, E, K, w_gu, w_dn, I, scale, logits, ids, w, off,
+        #  sorted, slot_pos, residual, rdt, out_f32, out_act, odt, ws, ws_bytes, stream)
+        return f(x, xdt, T, H, wr, None, None, E, K, A, A, I, A, logits, A, A, A, A, A, None, 0,
+                 out, act, odt, ws_, wsb, None)
+    assert call(T=9) == UNS                  # more than 8 tokens
+    assert call(T=8, K=16, E=128) == UNS     # more than 64 slots
+    assert call(H=2848) == UNS               # 89 blocks per gate/up row: odd
+    assert call(I=736) == UNS                # 23 blocks per down row: odd
+    assert call(xdt=3) == UNS
+    assert call(T=0, x=None) == OK
+    assert call(x=None) == NULL
+    assert call(out=None) == NULL             # no output
+    assert call(logits=None) == NULL
+    assert call(ws_=None) == WS
+    assert call(wsb=16) == WS
+    assert call(x=MIS) == ALIGN
+    assert call(E=300) == SHAPE
+
+
 def test_combine_and_rmsnorm_validation():
     f = lib.moe_combine
     # (y, slot_pos, ids, w, scale, T, K, H, residual, rdt, out_f32, out_act, odt, stream)
