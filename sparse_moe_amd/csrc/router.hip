@@ -225,11 +225,14 @@ __global__ __launch_bounds__(256) void route_small(const void* __restrict__ x, i
                                (bias ? bias[e] : 0.f));
     }
     __shared__ int s_last;
-    drain_stores();
-    __syncthreads();  // this workgroup's logits are complete
+    // The logits are stored by threads t < T <= 8, all in wave 0, which also
+    // makes the count: its release (agent scope) orders them before the
+    // increment, and the last workgroup's acquire fence (after it has seen
+    // every other increment) orders its reads after them.
     if (threadIdx.x == 0) {
-        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old == (int)gridDim.x - 1);
+        if (s_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
     if (!s_last) return;
