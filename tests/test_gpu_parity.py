@@ -241,3 +241,24 @@ def test_mfma_tile_size_boundaries(I):
     lg[np.arange(T), owner] += 10.0
     g, res = _run(L, logits_in=lg)
     assert np.array_equal(np.diff(g["offsets"]), np.array(counts)), np.diff(g["offsets"])
+
+
+def test_mfma_tile_boundaries_among_many_experts():
+    # The slot counts above (1, 32, 33, 64, 65, 96, 97, 129) among 128 more
+    # experts of 384 slots each (three full tiles): the tile numbering and the
+    # XCD runs over a few hundred tiles, with every tile variant present.
+    # Injected logits fix every token's expert; outputs are checked on the first
+    # and last token of the eight boundary experts and of a few others.
+    counts = [1, 32, 33, 64, 65, 96, 97, 129] + [384] * 128
+    T, E = sum(counts), len(counts)
+    spec = synth.LayerSpec("tile-bounds-many", H=256, E=E, K=1, I=512, T=T, act="bf16",
+                           router_std=1 / 16, seed=37)
+    L = synth.make_layer(spec)
+    rng = np.random.default_rng(41)
+    owner = rng.permutation(np.repeat(np.arange(E), counts))
+    lg = (rng.standard_normal((T, E)) * 0.1).astype(np.float32)
+    lg[np.arange(T), owner] += 10.0
+    sample = np.concatenate([np.nonzero(owner == e)[0][[0, -1]] for e in range(8)] +
+                            [np.nonzero(owner == e)[0][[0, -1]] for e in (8, 70, E - 1)])
+    g, res = _run(L, logits_in=lg, token_sample=np.unique(sample))
+    assert np.array_equal(np.diff(g["offsets"]), np.array(counts))
