@@ -87,16 +87,40 @@ MOE_DEV f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Tile lookup.  Slot tiles are numbered expert by expert, ceil(count/MT) per
-// expert; each slot tile has n_tiles column tiles.  The grid is
-// an upper bound on the tile count, so the numbering is made once the real
-// count is known: the tiles are cut into 8 equal runs of consecutive numbers,
-// run x going to the workgroups that the dispatcher places on XCD x (block
-// numbers congruent to x mod 8).  The column tiles of one slot tile, and the
-// next slot tile of the same expert, thus share an XCD's L2, and every XCD
-// gets an equal share however many tiles there are.  Wave 0 scans the expert
-// counts (up to 4 experts per lane); returns false for a workgroup without a
-// tile.
+// Tile lookup.  Slot tiles cover an expert's slots MT at a time (the last one
+// partial); each slot tile has n_tiles column tiles.  The grid is an upper
+// bound on the tile count, so the numbering is made once the real count is
+// known; the column tiles of one slot tile always take consecutive block
+// numbers of one XCD (blocks congruent to x mod 8 run on XCD x), so they share
+// that XCD's L2.
+//
+//  * Many tiles (more than FFN_MFMA_LPT_UNITS workgroups): slot tiles in
+//    expert order, the sequence cut into 8 equal runs of consecutive numbers,
+//    run x for XCD x, so the next slot tile of the same expert also shares the
+//    XCD's L2 (its weights).
+//  * Few tiles (a grid of about two rounds of resident workgroups or less, as
+//    with a few hundred tokens over many experts): how long the kernel takes
+//    is decided by how the tiles pack, and a tile's time grows with its slot
+//    count.  The slot tiles are ranked longest first (tiles of 97-128 slots,
+//    then 65-96, 33-64 and 1-32; expert order within a class) and rank r goes
+//    to XCD r mod 8, so every XCD starts its long tiles first and the short
+//    ones fill in behind them.
+//
+// Wave 0 scans the expert counts (up to 4 experts per lane); returns false
+// for a workgroup without a tile.
+constexpr int FFN_MFMA_LPT_UNITS = 1024;
+
+MOE_DEV int tile_class(int size) { return size > 96 ? 0 : size > 64 ? 1 : size > 32 ? 2 : 3; }
+
+MOE_DEV int scan_incl(int v, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(v, d);
+        if (lane >= d) v += u;
+    }
+    return v;
+}
+
 __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
                           int n_tiles, int* s_res, int& e_out, int& base, int& cnt, int& ntile) {
     if (threadIdx.x < 64) {
@@ -109,30 +133,81 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
             t[q] = (c[q] + MT - 1) / MT;
             tot += t[q];
         }
-        int incl = tot;
+        const int incl = scan_incl(tot, lane);
+        const int R = __shfl(incl, 63);  // slot tiles
+        const int total = R * n_tiles;
+        // this lane's find: expert, its slot tile, column tile
+        int e_sel = -1, k_sel = 0, c_sel = 0, nt_sel = 0;
+        if (total > FFN_MFMA_LPT_UNITS) {
+            const int per_xcd = (total + 7) >> 3;
+            const int lin = (bid & 7) * per_xcd + (bid >> 3);
+            const bool have = (bid >> 3) < per_xcd && lin < total;
+            const int tile = have ? lin / n_tiles : -1;
+            int run = incl - tot;
 #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int v = __shfl_up(incl, d);
-            if (lane >= d) incl += v;
-        }
-        const int total = __shfl(incl, 63) * n_tiles;
-        const int per_xcd = (total + 7) >> 3;
-        const int lin = (bid & 7) * per_xcd + (bid >> 3);
-        const bool have = (bid >> 3) < per_xcd && lin < total;
-        const int tile = have ? lin / n_tiles : -1;
-        int run = incl - tot;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (tile >= run && tile < run + t[q]) {
-                const int e = lane * 4 + q, k = tile - run;
-                s_res[0] = e;
-                s_res[1] = offsets[e] + k * MT;
-                s_res[2] = min(MT, c[q] - k * MT);
-                s_res[3] = lin - tile * n_tiles;
+            for (int q = 0; q < 4; ++q) {
+                if (tile >= run && tile < run + t[q]) {
+                    e_sel = lane * 4 + q;
+                    k_sel = tile - run;
+                    c_sel = c[q];
+                    nt_sel = lin - tile * n_tiles;
+                }
+                run += t[q];
             }
-            run += t[q];
+        } else {
+            // tiles per class: class 0 holds an expert's full tiles and a
+            // remainder of 97-127 slots, classes 1-3 the remainder (if any)
+            int n0[4], rc[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int rem = c[q] % MT, cls = rem ? tile_class(rem) : -1;
+                n0[q] = c[q] / MT + (cls == 0 ? 1 : 0);
+                rc[q] = cls > 0 ? cls : -1;
+            }
+            auto lane_count = [&](int k) {
+                int s = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) s += k == 0 ? n0[q] : (rc[q] == k ? 1 : 0);
+                return s;
+            };
+            // inclusive scans of the class counts, two 16-bit fields per int (in
+            // this branch a class holds at most R <= FFN_MFMA_LPT_UNITS tiles)
+            const int s01 = scan_incl(lane_count(0) + (lane_count(1) << 16), lane);
+            const int s23 = scan_incl(lane_count(2) + (lane_count(3) << 16), lane);
+            const int a01 = __shfl(s01, 63), a23 = __shfl(s23, 63);
+            const int tot0 = a01 & 0xFFFF, tot1 = a01 >> 16, tot2 = a23 & 0xFFFF;
+            const int x = bid & 7, qpos = bid >> 3;
+            const int s8 = qpos / n_tiles;
+            const int r = s8 * 8 + x;  // rank of this block's slot tile
+            if (r < R) {
+                const int k = r < tot0 ? 0 : r < tot0 + tot1 ? 1 : r < tot0 + tot1 + tot2 ? 2 : 3;
+                const int idx = r - (k >= 1 ? tot0 : 0) - (k >= 2 ? tot1 : 0) - (k >= 3 ? tot2 : 0);
+                const int inclk = k == 0 ? (s01 & 0xFFFF) : k == 1 ? (s01 >> 16)
+                                : k == 2 ? (s23 & 0xFFFF) : (s23 >> 16);
+                int run = inclk - lane_count(k);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int nq = k == 0 ? n0[q] : (rc[q] == k ? 1 : 0);
+                    if (idx >= run && idx < run + nq) {
+                        e_sel = lane * 4 + q;
+                        k_sel = k == 0 ? idx - run : c[q] / MT;
+                        c_sel = c[q];
+                        nt_sel = qpos - s8 * n_tiles;
+                    }
+                    run += nq;
+                }
+            }
         }
-        if (lane == 63 && !have) s_res[0] = -1;
+        if (e_sel >= 0) {
+            s_res[0] = e_sel;
+            s_res[1] = offsets[e_sel] + k_sel * MT;
+            s_res[2] = min(MT, c_sel - k_sel * MT);
+            s_res[3] = nt_sel;
+        }
+        // exactly one lane finds the tile; without one lane 63 marks the block
+        // (the whole wave votes)
+        const bool found = __ballot(e_sel >= 0) != 0;
+        if (lane == 63 && !found) s_res[0] = -1;
     }
     __syncthreads();
     e_out = s_res[0];
@@ -142,11 +217,15 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
     return e_out >= 0;
 }
 
-// MODE 0: gate/up.  act = permuted x [T][H], csum = -1.5 * block sums [T][H/32],
-//         W = w_gate_up, rows_e = 2I, ncols = I; writes h (permuted) and its
-//         block sums.
-// MODE 1: down.     act = permuted h [N][I], csum [N][I/32], W = w_down,
-//         rows_e = ncols = H; writes y_sorted.
+// MODE 0: gate/up.  act = permuted x [T][apitch], csum = -1.5 * block sums of
+//         the slots' tokens, block-major in slot order [H/32][cs_stride = N],
+//         W = w_gate_up, rows_e = 2I, ncols = I; writes h (permuted, rows
+//         hpitch apart) and its block sums (block-major, [I/32][N]).
+// MODE 1: down.     act = permuted h [N][apitch], csum [I/32][cs_stride = N],
+//         W = w_down, rows_e = ncols = H; writes y_sorted.
+// The block sums of a tile's slots are contiguous for each block, so a pair of
+// blocks costs a few cache-line requests (one 4-byte request per slot in a
+// token-major layout: a quarter of all requests for a thirtieth of the bytes).
 // Requires an even number of blocks per row (H and I multiples of 64), so that
 // every pair of blocks starts on a dword boundary.
 //
@@ -184,7 +263,8 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
 template <int MODE, bool BUF>
 __global__ __launch_bounds__(256) void ffn_mfma(
     const uint16_t* __restrict__ act, const float* __restrict__ csum, const uint8_t* __restrict__ W,
-    int nb, int rows_e, int ncols, int n_tiles, const int32_t* __restrict__ offsets,
+    int nb, int apitch, int rows_e, int ncols, int cs_stride, int hpitch, int n_tiles,
+    const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_slots, int K, int E, uint16_t* __restrict__ h_out,
     float* __restrict__ hsum_out, float* __restrict__ y_out) {
     __shared__ __attribute__((aligned(16))) uint8_t a0[2 * MT * 64], a1[2 * MT * 64];
@@ -246,9 +326,7 @@ __global__ __launch_bounds__(256) void ffn_mfma(
     int64_t cbyte0;  // byte offset in csum
     {
         const int r = 64 * (wave & 1) + lane;
-        const int p = base + min(r, cnt - 1);
-        const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
-        cbyte0 = (arow * nb + (wave >> 1)) * 4;
+        cbyte0 = ((int64_t)(wave >> 1) * cs_stride + base + min(r, cnt - 1)) * 4;
     }
     // buffer resources (unbounded: every offset stays inside its buffer); the
     // fourth descriptor word selects 32-bit data, as untyped loads need
@@ -287,7 +365,7 @@ __global__ __launch_bounds__(256) void ffn_mfma(
             const int p = base + min(r, cnt - 1);
             const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
             const int chunk = (lane & 3) ^ ((r >> 2) & 3);
-            abyte[i] = (arow * nb * 32 + blk * 32 + 8 * chunk) * 2;
+            abyte[i] = (arow * apitch + blk * 32 + 8 * chunk) * 2;
             adst[i] = blk * AROWS * 64 + rg * 1024;
         }
         // block sums: a heavy stage takes block w >> 1 of rows 64 (w & 1) + lane
@@ -298,13 +376,12 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         int cdst = 64 * wave;
         if constexpr (LIGHT) {
             const int r = lane & 31;
-            const int p = base + min(r, cnt - 1);
-            const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
-            cbyte = (arow * nb + (lane >> 5)) * 4;
+            cbyte = ((int64_t)(lane >> 5) * cs_stride + base + min(r, cnt - 1)) * 4;
             cdst = 0;
         }
-        // pair j: activations 128 bytes, block sums 8 bytes and weights 36 bytes
-        // further on
+        // pair j: activations 128 bytes, block sums two blocks (2 cs_stride
+        // floats) and weights 36 bytes further on
+        const int cpair = 8 * cs_stride;
         auto issue = [&](const StageRef& S, int j) {
             if constexpr (BUF) {
 #pragma unroll
@@ -312,7 +389,7 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(r_act, (lds_void_t*)(S.a + adst[i]), 16,
                                                              (int)abyte[i], 128 * j, 0, 0);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(r_cs, (lds_void_t*)(S.c + cdst), 4,
-                                                         (int)cbyte, 8 * j, 0, 0);
+                                                         (int)cbyte, cpair * j, 0, 0);
 #pragma unroll
                 for (int i = 0; i < 3; ++i)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -325,7 +402,7 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                 for (int i = 0; i < NA; ++i)
                     __builtin_amdgcn_global_load_lds((glb_void_t*)(act_b + abyte[i] + 128 * j),
                                                      (lds_void_t*)(S.a + adst[i]), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((glb_void_t*)(cs_b + cbyte + 8 * j),
+                __builtin_amdgcn_global_load_lds((glb_void_t*)(cs_b + cbyte + (int64_t)cpair * j),
                                                  (lds_void_t*)(S.c + cdst), 4, 0, 0);
 #pragma unroll
                 for (int i = 0; i < 3; ++i)
@@ -442,7 +519,6 @@ __global__ __launch_bounds__(256) void ffn_mfma(
             // fragment's 16 rows of 64 bytes go through a stage array of the wave's
             // own (rows 80 bytes apart, so the 4 lane groups' writes fall in
             // different banks) and leave as one 16-byte store per lane.
-            const int I = ncols, nbh = I >> 5;
             const int hblk = c0 >> 5;
             constexpr int RB = 80;
             static_assert(MT * RB <= NT * 48 && NT * 48 <= 2 * MT * 64, "h staging fits");
@@ -468,11 +544,11 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                         s += dpp_mov_f32<DPP_QUAD_XOR2>(s);
                         s += dpp_mov_f32<DPP_ROW_HALF_MIRROR>(s);
                         s += dpp_mov_f32<DPP_ROW_MIRROR>(s);
-                        if (ok && l16 == 0) hsum_out[p * nbh + hblk] = -1.5f * s;
+                        if (ok && l16 == 0) hsum_out[(int64_t)hblk * cs_stride + p] = -1.5f * s;
                     }
                     const int r = mf * 16 + (lane >> 2), ch = lane & 3;
                     const uint4 v = *(const uint4*)(R + r * RB + 16 * ch);
-                    if (r < cnt) *(uint4*)(h_out + (int64_t)(base + r) * I + hblk * 32 + 8 * ch) = v;
+                    if (r < cnt) *(uint4*)(h_out + (int64_t)(base + r) * hpitch + hblk * 32 + 8 * ch) = v;
                 }
             }
         } else {
@@ -518,15 +594,16 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         run(std::integral_constant<int, 8>{});
 }
 
-// Activations -> MFMA block order, plus -1.5 * block sums.  Four lanes per
-// 32-element block, one 16-byte quarter each (loads and stores of a wave are
-// contiguous): output chunk c of a block holds elements 4c..4c+3 of quarter
-// c >> 1 and elements 4c+16..4c+19 of quarter (c >> 1) + 2, which reach lane
-// c through quad DPP moves.  The block sum is each lane's 8 values in order,
-// then the quad's four partial sums.
-__global__ __launch_bounds__(256) void ffn_mfma_prep(const uint16_t* __restrict__ x, int64_t nblocks,
-                                                     uint16_t* __restrict__ xp,
+// Activations -> MFMA block order, plus -1.5 * block sums, block-major
+// ([nb][T]).  Four lanes per 32-element block, one 16-byte quarter each (loads
+// and stores of a wave are contiguous): output chunk c of a block holds
+// elements 4c..4c+3 of quarter c >> 1 and elements 4c+16..4c+19 of quarter
+// (c >> 1) + 2, which reach lane c through quad DPP moves.  The block sum is
+// each lane's 8 values in order, then the quad's four partial sums.
+__global__ __launch_bounds__(256) void ffn_mfma_prep(const uint16_t* __restrict__ x, int64_t T, int nb,
+                                                     int pitch, uint16_t* __restrict__ xp,
                                                      float* __restrict__ xs) {
+    const int64_t nblocks = T * nb;
     const int64_t nq = nblocks * 4;
     const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const u32x4 v = reinterpret_cast<const u32x4*>(x)[min(q, nq - 1)];
@@ -558,18 +635,38 @@ __global__ __launch_bounds__(256) void ffn_mfma_prep(const uint16_t* __restrict_
     o.z = (A >> 16) | (B & 0xFFFF0000u);
     o.w = (C >> 16) | (D & 0xFFFF0000u);
     if (q < nq) {
-        reinterpret_cast<u32x4*>(xp)[q] = o;
-        if (c == 0) xs[q >> 2] = -1.5f * s;
+        const int64_t t = q / (4 * nb), qq = q - t * 4 * nb;
+        reinterpret_cast<u32x4*>(xp + t * pitch)[qq] = o;
+        if (c == 0) xs[(qq >> 2) * T + t] = -1.5f * s;
     }
+}
+
+// Block sums of the slots' tokens, block-major in slot order:
+// cs[b][p] = xs[b][sorted_slots[p] / K] (consecutive threads write consecutive
+// slots of one block).
+__global__ __launch_bounds__(256) void ffn_mfma_sums_gather(const float* __restrict__ xs, int64_t T,
+                                                            int nb, const int32_t* __restrict__ sorted_slots,
+                                                            int K, int N, float* __restrict__ cs) {
+    const int p = blockIdx.x * 256 + threadIdx.x;
+    if (p >= N) return;
+    const int64_t t = sorted_slots[p] / K;
+    for (int b = blockIdx.y; b < nb; b += gridDim.y) cs[(int64_t)b * N + p] = xs[(int64_t)b * T + t];
 }
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 }  // namespace
 
+// Row pitch (elements) of a staged activation matrix with `cols` bf16 columns
+// (a multiple of 64): an odd number of 128-byte lines.  Tiles gather rows of
+// one block pair at a time; with an even line count (5,632 bytes for 2,816
+// columns: 44 lines) those rows fall on a quarter of the L2 channels.
+static int act_pitch(int cols) { return ((cols * 2 / 128) & 1) ? cols : cols + 64; }
+
 size_t ffn_mfma_ws_bytes(int64_t T, int H, int I, int64_t N) {
-    return align256((size_t)T * H * 2) + align256((size_t)T * (H / 32) * 4) +
-           align256((size_t)N * I * 2) + align256((size_t)N * (I / 32) * 4);
+    return align256((size_t)T * act_pitch(H) * 2) + align256((size_t)T * (H / 32) * 4) +
+           align256((size_t)N * (H / 32) * 4) + align256((size_t)N * act_pitch(I) * 2) +
+           align256((size_t)N * (I / 32) * 4);
 }
 
 // Buffer loads take 32-bit offsets: every byte of an activation buffer of this
@@ -582,63 +679,77 @@ hipError_t launch_ffn_mfma(const void* x, int64_t T, int H, const uint8_t* w_gat
                            const int32_t* offsets, const int32_t* sorted_slots, void* ws,
                            float* y_sorted, hipStream_t st) {
     uint8_t* p = (uint8_t*)ws;
+    const int xpitch = act_pitch(H), hpitch = act_pitch(I);
     uint16_t* xp = (uint16_t*)p;
-    p += align256((size_t)T * H * 2);
+    p += align256((size_t)T * xpitch * 2);
     float* xs = (float*)p;
     p += align256((size_t)T * (H / 32) * 4);
+    float* cs = (float*)p;
+    p += align256((size_t)N * (H / 32) * 4);
     uint16_t* hp = (uint16_t*)p;
-    p += align256((size_t)N * I * 2);
+    p += align256((size_t)N * hpitch * 2);
     float* hs = (float*)p;
 
     const int64_t nblk = T * (H / 32);
-    ffn_mfma_prep<<<(unsigned)((4 * nblk + 255) / 256), 256, 0, st>>>((const uint16_t*)x, nblk, xp, xs);
+    ffn_mfma_prep<<<(unsigned)((4 * nblk + 255) / 256), 256, 0, st>>>((const uint16_t*)x, T, H / 32, xpitch,
+                                                                      xp, xs);
+    ffn_mfma_sums_gather<<<dim3((unsigned)((N + 255) / 256), (unsigned)min(H / 32, 8)), 256, 0, st>>>(
+        xs, T, H / 32, sorted_slots, K, N, cs);
 
     // slot tiles: sum over experts of ceil(count / MT) <= N / MT + (experts hit);
     // the workgroups past the real count exit at once
     const int mtiles = N / MT + min(E, N);
+    // grid: room for ceil(mtiles / 8) slot tiles per XCD with all their column
+    // tiles (either numbering fits in it)
     {
         const int n_tiles = (I + NT / 2 - 1) / (NT / 2);
-        const int total = (mtiles * n_tiles + 7) / 8 * 8;
-        if (buf_ok((size_t)T * H * 2))
-            ffn_mfma<0, true><<<total, 256, 0, st>>>(xp, xs, w_gate_up, H / 32, 2 * I, I, n_tiles,
-                                                     offsets, sorted_slots, K, E, hp, hs, nullptr);
+        const int total = (mtiles + 7) / 8 * 8 * n_tiles;
+        if (buf_ok((size_t)T * xpitch * 2))
+            ffn_mfma<0, true><<<total, 256, 0, st>>>(xp, cs, w_gate_up, H / 32, xpitch, 2 * I, I, N,
+                                                     hpitch, n_tiles, offsets, sorted_slots, K, E, hp,
+                                                     hs, nullptr);
         else
-            ffn_mfma<0, false><<<total, 256, 0, st>>>(xp, xs, w_gate_up, H / 32, 2 * I, I, n_tiles,
-                                                      offsets, sorted_slots, K, E, hp, hs, nullptr);
+            ffn_mfma<0, false><<<total, 256, 0, st>>>(xp, cs, w_gate_up, H / 32, xpitch, 2 * I, I, N,
+                                                      hpitch, n_tiles, offsets, sorted_slots, K, E, hp,
+                                                      hs, nullptr);
     }
     {
         const int n_tiles = (H + NT - 1) / NT;
-        const int total = (mtiles * n_tiles + 7) / 8 * 8;
-        if (buf_ok((size_t)N * I * 2))
-            ffn_mfma<1, true><<<total, 256, 0, st>>>(hp, hs, w_down, I / 32, H, H, n_tiles, offsets,
-                                                     sorted_slots, K, E, nullptr, nullptr, y_sorted);
+        const int total = (mtiles + 7) / 8 * 8 * n_tiles;
+        if (buf_ok((size_t)N * hpitch * 2))
+            ffn_mfma<1, true><<<total, 256, 0, st>>>(hp, hs, w_down, I / 32, hpitch, H, H, N, 0, n_tiles,
+                                                     offsets, sorted_slots, K, E, nullptr, nullptr,
+                                                     y_sorted);
         else
-            ffn_mfma<1, false><<<total, 256, 0, st>>>(hp, hs, w_down, I / 32, H, H, n_tiles, offsets,
-                                                      sorted_slots, K, E, nullptr, nullptr, y_sorted);
+            ffn_mfma<1, false><<<total, 256, 0, st>>>(hp, hs, w_down, I / 32, hpitch, H, H, N, 0,
+                                                      n_tiles, offsets, sorted_slots, K, E, nullptr,
+                                                      nullptr, y_sorted);
     }
     return hipGetLastError();
 }
 
 size_t linear_mfma_ws_bytes(int64_t T, int H) {
-    return align256((size_t)T * H * 2) + align256((size_t)T * (H / 32) * 4);
+    return align256((size_t)T * act_pitch(H) * 2) + align256((size_t)T * (H / 32) * 4);
 }
 
 hipError_t launch_linear_mfma(const void* x, int64_t T, int H, const uint8_t* W, int R,
                               const int32_t* offsets, const int32_t* slots, void* ws, float* y,
                               hipStream_t st) {
+    const int xpitch = act_pitch(H);
     uint16_t* xp = (uint16_t*)ws;
-    float* xs = (float*)((uint8_t*)ws + align256((size_t)T * H * 2));
+    float* xs = (float*)((uint8_t*)ws + align256((size_t)T * xpitch * 2));
     const int64_t nblk = T * (H / 32);
-    ffn_mfma_prep<<<(unsigned)((4 * nblk + 255) / 256), 256, 0, st>>>((const uint16_t*)x, nblk, xp, xs);
+    ffn_mfma_prep<<<(unsigned)((4 * nblk + 255) / 256), 256, 0, st>>>((const uint16_t*)x, T, H / 32, xpitch,
+                                                                      xp, xs);
     const int N = (int)T, mtiles = N / MT + 1;
     const int n_tiles = (R + NT - 1) / NT;
-    const int total = (mtiles * n_tiles + 7) / 8 * 8;
-    if (buf_ok((size_t)T * H * 2))
-        ffn_mfma<1, true><<<total, 256, 0, st>>>(xp, xs, W, H / 32, R, R, n_tiles, offsets, slots, 1,
-                                                 1, nullptr, nullptr, y);
+    const int total = (mtiles + 7) / 8 * 8 * n_tiles;
+    if (buf_ok((size_t)T * xpitch * 2))
+        ffn_mfma<1, true><<<total, 256, 0, st>>>(xp, xs, W, H / 32, xpitch, R, R, N, 0, n_tiles,
+                                                 offsets, slots, 1, 1, nullptr, nullptr, y);
     else
-        ffn_mfma<1, false><<<total, 256, 0, st>>>(xp, xs, W, H / 32, R, R, n_tiles, offsets, slots,
-                                                  1, 1, nullptr, nullptr, y);
+        ffn_mfma<1, false><<<total, 256, 0, st>>>(xp, xs, W, H / 32, xpitch, R, R, N, 0, n_tiles,
+                                                  offsets, slots, 1, 1, nullptr, nullptr, y);
     return hipGetLastError();
 }
 

@@ -262,3 +262,21 @@ def test_mfma_tile_boundaries_among_many_experts():
                             [np.nonzero(owner == e)[0][[0, -1]] for e in (8, 70, E - 1)])
     g, res = _run(L, logits_in=lg, token_sample=np.unique(sample))
     assert np.array_equal(np.diff(g["offsets"]), np.array(counts))
+
+
+@pytest.mark.parametrize("I", [512, 704])
+def test_mfma_longest_first_numbering(I):
+    # A grid of a few dozen tiles, so both grouped-GEMM launches rank the slot
+    # tiles longest first: experts with tiles of every size class (1-32, 33-64,
+    # 65-96 and 97-128 slots, full tiles, none), every token checked.
+    counts = [1, 20, 33, 50, 65, 90, 97, 120, 128, 129, 200, 256, 300, 5, 0, 77]
+    T, E = sum(counts), len(counts)
+    spec = synth.LayerSpec("longest-first-I%d" % I, H=256, E=E, K=1, I=I, T=T, act="bf16",
+                           router_std=1 / 16, seed=43)
+    L = synth.make_layer(spec)
+    rng = np.random.default_rng(47)
+    owner = rng.permutation(np.repeat(np.arange(E), counts))
+    lg = (rng.standard_normal((T, E)) * 0.1).astype(np.float32)
+    lg[np.arange(T), owner] += 10.0
+    g, res = _run(L, logits_in=lg)
+    assert np.array_equal(np.diff(g["offsets"]), np.array(counts))
