@@ -98,7 +98,7 @@ MOE_DEV f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
 //    expert order, the sequence cut into 8 equal runs of consecutive numbers,
 //    run x for XCD x, so the next slot tile of the same expert also shares the
 //    XCD's L2 (its weights).
-//  * Few tiles (a grid of about two rounds of resident workgroups or less, as
+//  * Few tiles (a grid of about three rounds of resident workgroups or less, as
 //    with a few hundred tokens over many experts): how long the kernel takes
 //    is decided by how the tiles pack, and a tile's time grows with its slot
 //    count.  The slot tiles are ranked longest first (tiles of 97-128 slots,
@@ -108,7 +108,7 @@ MOE_DEV f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
 //
 // Wave 0 scans the expert counts (up to 4 experts per lane); returns false
 // for a workgroup without a tile.
-constexpr int FFN_MFMA_LPT_UNITS = 1024;
+constexpr int FFN_MFMA_LPT_UNITS = 1536;
 
 MOE_DEV int tile_class(int size) { return size > 96 ? 0 : size > 64 ? 1 : size > 32 ? 2 : 3; }
 
@@ -217,15 +217,15 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
     return e_out >= 0;
 }
 
-// MODE 0: gate/up.  act = permuted x [T][apitch], csum = -1.5 * block sums of
-//         the slots' tokens, block-major in slot order [H/32][cs_stride = N],
-//         W = w_gate_up, rows_e = 2I, ncols = I; writes h (permuted, rows
-//         hpitch apart) and its block sums (block-major, [I/32][N]).
-// MODE 1: down.     act = permuted h [N][apitch], csum [I/32][cs_stride = N],
-//         W = w_down, rows_e = ncols = H; writes y_sorted.
-// The block sums of a tile's slots are contiguous for each block, so a pair of
-// blocks costs a few cache-line requests (one 4-byte request per slot in a
-// token-major layout: a quarter of all requests for a thirtieth of the bytes).
+// MODE 0: gate/up.  act = staged x [T][apitch] (rows gathered through the
+//         slots' tokens), csum = -1.5 * block sums per token [T][H/32]
+//         (cs_row = H/32, cs_blk = 1), W = w_gate_up, rows_e = 2I, ncols = I;
+//         writes h (slot order, rows hpitch apart) and its block sums
+//         block-major [I/32][hs_blk = N].
+// MODE 1: down.     act = h [N][apitch], csum = its block sums [I/32][N]
+//         (cs_row = 1, cs_blk = N), W = w_down, rows_e = ncols = H; writes
+//         y_sorted.
+// Sum (row, block) is at csum[row * cs_row + block * cs_blk].
 // Requires an even number of blocks per row (H and I multiples of 64), so that
 // every pair of blocks starts on a dword boundary.
 //
@@ -263,7 +263,8 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
 template <int MODE, bool BUF>
 __global__ __launch_bounds__(256) void ffn_mfma(
     const uint16_t* __restrict__ act, const float* __restrict__ csum, const uint8_t* __restrict__ W,
-    int nb, int apitch, int rows_e, int ncols, int cs_stride, int hpitch, int n_tiles,
+    int nb, int apitch, int rows_e, int ncols, int cs_row, int cs_blk, int hpitch, int hs_blk,
+    int n_tiles,
     const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_slots, int K, int E, uint16_t* __restrict__ h_out,
     float* __restrict__ hsum_out, float* __restrict__ y_out) {
@@ -326,7 +327,9 @@ __global__ __launch_bounds__(256) void ffn_mfma(
     int64_t cbyte0;  // byte offset in csum
     {
         const int r = 64 * (wave & 1) + lane;
-        cbyte0 = ((int64_t)(wave >> 1) * cs_stride + base + min(r, cnt - 1)) * 4;
+        const int p = base + min(r, cnt - 1);
+        const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
+        cbyte0 = (arow * cs_row + (int64_t)(wave >> 1) * cs_blk) * 4;
     }
     // buffer resources (unbounded: every offset stays inside its buffer); the
     // fourth descriptor word selects 32-bit data, as untyped loads need
@@ -376,12 +379,14 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         int cdst = 64 * wave;
         if constexpr (LIGHT) {
             const int r = lane & 31;
-            cbyte = ((int64_t)(lane >> 5) * cs_stride + base + min(r, cnt - 1)) * 4;
+            const int p = base + min(r, cnt - 1);
+            const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
+            cbyte = (arow * cs_row + (int64_t)(lane >> 5) * cs_blk) * 4;
             cdst = 0;
         }
-        // pair j: activations 128 bytes, block sums two blocks (2 cs_stride
+        // pair j: activations 128 bytes, block sums two blocks (2 cs_blk
         // floats) and weights 36 bytes further on
-        const int cpair = 8 * cs_stride;
+        const int cpair = 8 * cs_blk;
         auto issue = [&](const StageRef& S, int j) {
             if constexpr (BUF) {
 #pragma unroll
@@ -544,7 +549,7 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                         s += dpp_mov_f32<DPP_QUAD_XOR2>(s);
                         s += dpp_mov_f32<DPP_ROW_HALF_MIRROR>(s);
                         s += dpp_mov_f32<DPP_ROW_MIRROR>(s);
-                        if (ok && l16 == 0) hsum_out[(int64_t)hblk * cs_stride + p] = -1.5f * s;
+                        if (ok && l16 == 0) hsum_out[(int64_t)hblk * hs_blk + p] = -1.5f * s;
                     }
                     const int r = mf * 16 + (lane >> 2), ch = lane & 3;
                     const uint4 v = *(const uint4*)(R + r * RB + 16 * ch);
@@ -594,8 +599,8 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         run(std::integral_constant<int, 8>{});
 }
 
-// Activations -> MFMA block order, plus -1.5 * block sums, block-major
-// ([nb][T]).  Four lanes per 32-element block, one 16-byte quarter each (loads
+// Activations -> MFMA block order (rows pitch apart), plus -1.5 * block sums
+// ([T][nb]).  Four lanes per 32-element block, one 16-byte quarter each (loads
 // and stores of a wave are contiguous): output chunk c of a block holds
 // elements 4c..4c+3 of quarter c >> 1 and elements 4c+16..4c+19 of quarter
 // (c >> 1) + 2, which reach lane c through quad DPP moves.  The block sum is
@@ -637,20 +642,8 @@ __global__ __launch_bounds__(256) void ffn_mfma_prep(const uint16_t* __restrict_
     if (q < nq) {
         const int64_t t = q / (4 * nb), qq = q - t * 4 * nb;
         reinterpret_cast<u32x4*>(xp + t * pitch)[qq] = o;
-        if (c == 0) xs[(qq >> 2) * T + t] = -1.5f * s;
+        if (c == 0) xs[q >> 2] = -1.5f * s;
     }
-}
-
-// Block sums of the slots' tokens, block-major in slot order:
-// cs[b][p] = xs[b][sorted_slots[p] / K] (consecutive threads write consecutive
-// slots of one block).
-__global__ __launch_bounds__(256) void ffn_mfma_sums_gather(const float* __restrict__ xs, int64_t T,
-                                                            int nb, const int32_t* __restrict__ sorted_slots,
-                                                            int K, int N, float* __restrict__ cs) {
-    const int p = blockIdx.x * 256 + threadIdx.x;
-    if (p >= N) return;
-    const int64_t t = sorted_slots[p] / K;
-    for (int b = blockIdx.y; b < nb; b += gridDim.y) cs[(int64_t)b * N + p] = xs[(int64_t)b * T + t];
 }
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
@@ -665,8 +658,7 @@ static int act_pitch(int cols) { return ((cols * 2 / 128) & 1) ? cols : cols + 6
 
 size_t ffn_mfma_ws_bytes(int64_t T, int H, int I, int64_t N) {
     return align256((size_t)T * act_pitch(H) * 2) + align256((size_t)T * (H / 32) * 4) +
-           align256((size_t)N * (H / 32) * 4) + align256((size_t)N * act_pitch(I) * 2) +
-           align256((size_t)N * (I / 32) * 4);
+           align256((size_t)N * act_pitch(I) * 2) + align256((size_t)N * (I / 32) * 4);
 }
 
 // Buffer loads take 32-bit offsets: every byte of an activation buffer of this
@@ -684,8 +676,6 @@ hipError_t launch_ffn_mfma(const void* x, int64_t T, int H, const uint8_t* w_gat
     p += align256((size_t)T * xpitch * 2);
     float* xs = (float*)p;
     p += align256((size_t)T * (H / 32) * 4);
-    float* cs = (float*)p;
-    p += align256((size_t)N * (H / 32) * 4);
     uint16_t* hp = (uint16_t*)p;
     p += align256((size_t)N * hpitch * 2);
     float* hs = (float*)p;
@@ -693,8 +683,6 @@ hipError_t launch_ffn_mfma(const void* x, int64_t T, int H, const uint8_t* w_gat
     const int64_t nblk = T * (H / 32);
     ffn_mfma_prep<<<(unsigned)((4 * nblk + 255) / 256), 256, 0, st>>>((const uint16_t*)x, T, H / 32, xpitch,
                                                                       xp, xs);
-    ffn_mfma_sums_gather<<<dim3((unsigned)((N + 255) / 256), (unsigned)min(H / 32, 8)), 256, 0, st>>>(
-        xs, T, H / 32, sorted_slots, K, N, cs);
 
     // slot tiles: sum over experts of ceil(count / MT) <= N / MT + (experts hit);
     // the workgroups past the real count exit at once
@@ -705,23 +693,23 @@ hipError_t launch_ffn_mfma(const void* x, int64_t T, int H, const uint8_t* w_gat
         const int n_tiles = (I + NT / 2 - 1) / (NT / 2);
         const int total = (mtiles + 7) / 8 * 8 * n_tiles;
         if (buf_ok((size_t)T * xpitch * 2))
-            ffn_mfma<0, true><<<total, 256, 0, st>>>(xp, cs, w_gate_up, H / 32, xpitch, 2 * I, I, N,
-                                                     hpitch, n_tiles, offsets, sorted_slots, K, E, hp,
+            ffn_mfma<0, true><<<total, 256, 0, st>>>(xp, xs, w_gate_up, H / 32, xpitch, 2 * I, I, H / 32, 1,
+                                                     hpitch, N, n_tiles, offsets, sorted_slots, K, E, hp,
                                                      hs, nullptr);
         else
-            ffn_mfma<0, false><<<total, 256, 0, st>>>(xp, cs, w_gate_up, H / 32, xpitch, 2 * I, I, N,
-                                                      hpitch, n_tiles, offsets, sorted_slots, K, E, hp,
+            ffn_mfma<0, false><<<total, 256, 0, st>>>(xp, xs, w_gate_up, H / 32, xpitch, 2 * I, I, H / 32, 1,
+                                                      hpitch, N, n_tiles, offsets, sorted_slots, K, E, hp,
                                                       hs, nullptr);
     }
     {
         const int n_tiles = (H + NT - 1) / NT;
         const int total = (mtiles + 7) / 8 * 8 * n_tiles;
         if (buf_ok((size_t)N * hpitch * 2))
-            ffn_mfma<1, true><<<total, 256, 0, st>>>(hp, hs, w_down, I / 32, hpitch, H, H, N, 0, n_tiles,
-                                                     offsets, sorted_slots, K, E, nullptr, nullptr,
+            ffn_mfma<1, true><<<total, 256, 0, st>>>(hp, hs, w_down, I / 32, hpitch, H, H, 1, N, 0, 0,
+                                                     n_tiles, offsets, sorted_slots, K, E, nullptr, nullptr,
                                                      y_sorted);
         else
-            ffn_mfma<1, false><<<total, 256, 0, st>>>(hp, hs, w_down, I / 32, hpitch, H, H, N, 0,
+            ffn_mfma<1, false><<<total, 256, 0, st>>>(hp, hs, w_down, I / 32, hpitch, H, H, 1, N, 0, 0,
                                                       n_tiles, offsets, sorted_slots, K, E, nullptr,
                                                       nullptr, y_sorted);
     }
@@ -745,11 +733,11 @@ hipError_t launch_linear_mfma(const void* x, int64_t T, int H, const uint8_t* W,
     const int n_tiles = (R + NT - 1) / NT;
     const int total = (mtiles + 7) / 8 * 8 * n_tiles;
     if (buf_ok((size_t)T * xpitch * 2))
-        ffn_mfma<1, true><<<total, 256, 0, st>>>(xp, xs, W, H / 32, xpitch, R, R, N, 0, n_tiles,
-                                                 offsets, slots, 1, 1, nullptr, nullptr, y);
+        ffn_mfma<1, true><<<total, 256, 0, st>>>(xp, xs, W, H / 32, xpitch, R, R, H / 32, 1, 0, 0,
+                                                 n_tiles, offsets, slots, 1, 1, nullptr, nullptr, y);
     else
-        ffn_mfma<1, false><<<total, 256, 0, st>>>(xp, xs, W, H / 32, xpitch, R, R, N, 0, n_tiles,
-                                                  offsets, slots, 1, 1, nullptr, nullptr, y);
+        ffn_mfma<1, false><<<total, 256, 0, st>>>(xp, xs, W, H / 32, xpitch, R, R, H / 32, 1, 0, 0,
+                                                  n_tiles, offsets, slots, 1, 1, nullptr, nullptr, y);
     return hipGetLastError();
 }
 
