@@ -453,6 +453,102 @@ __global__ __launch_bounds__(NW * 64) void router_logits_mfma(const uint16_t* __
         }
 }
 
+// Few tiles (a few hundred tokens): 16 tokens x 16 EF experts per workgroup
+// (many workgroups: each CU's loads, not the arithmetic, set the pace), K
+// split over NW waves, and each wave issues the loads of PF K steps at a time
+// before their MFMAs.  Same split, same per-element order (hi, mid, lo per
+// step, steps in k order, waves' partial sums in wave order).
+template <int NW, int PF, int EF, bool RSC>
+__global__ __launch_bounds__(NW * 64) void router_logits_mfma_batch(
+    const uint16_t* __restrict__ x, int T, int H, const float* __restrict__ W,
+    const float* __restrict__ rsc, const float* __restrict__ bias, int E, float* __restrict__ logits) {
+    __shared__ f32x4 part[NW - 1][EF][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int t0 = blockIdx.x * 16;
+    const int e0 = blockIdx.y * 16 * EF;
+    const int nsteps = H >> 5;
+    const int k_begin = (nsteps * wave / NW) * 32, k_end = (nsteps * (wave + 1) / NW) * 32;
+    const uint16_t* xf = x + (int64_t)min(t0 + l16, T - 1) * H + 8 * g;
+    const float* wp[EF];
+#pragma unroll
+    for (int f = 0; f < EF; ++f) wp[f] = W + (int64_t)(e0 + 16 * f + l16) * H + 8 * g;
+    f32x4 acc[EF];
+#pragma unroll
+    for (int f = 0; f < EF; ++f) acc[f] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int kb = k_begin; kb < k_end; kb += 32 * PF) {
+        ru32x4 a[PF];
+        f32x4 p0[PF][EF], p1[PF][EF];
+        f32x4 s0[RSC ? PF : 1], s1[RSC ? PF : 1];
+#pragma unroll
+        for (int s = 0; s < PF; ++s) {
+            const int k = min(kb + 32 * s, k_end - 32);  // past the end: a step that is not used
+            a[s] = *(const ru32x4*)(xf + k);
+#pragma unroll
+            for (int f = 0; f < EF; ++f) {
+                p0[s][f] = *(const f32x4*)(wp[f] + k);
+                p1[s][f] = *(const f32x4*)(wp[f] + k + 4);
+            }
+            if constexpr (RSC) {
+                s0[s] = *(const f32x4*)(rsc + 8 * g + k);
+                s1[s] = *(const f32x4*)(rsc + 8 * g + k + 4);
+            }
+        }
+        // all of the batch's loads land here (otherwise the compiler moves each
+        // step's loads next to its MFMAs, one round trip per step)
+#pragma unroll
+        for (int s = 0; s < PF; ++s) {
+            asm volatile("" ::"v"(a[s]));
+#pragma unroll
+            for (int f = 0; f < EF; ++f) asm volatile("" ::"v"(p0[s][f]), "v"(p1[s][f]));
+            if constexpr (RSC) asm volatile("" ::"v"(s0[s]), "v"(s1[s]));
+        }
+#pragma unroll
+        for (int s = 0; s < PF; ++s) {
+            if (kb + 32 * s >= k_end) break;
+            ru32x4 hi[EF], mid[EF], lo[EF];
+#pragma unroll
+            for (int f = 0; f < EF; ++f) {
+                float wv[8] = {p0[s][f].x, p0[s][f].y, p0[s][f].z, p0[s][f].w,
+                               p1[s][f].x, p1[s][f].y, p1[s][f].z, p1[s][f].w};
+                if constexpr (RSC) {
+                    const float sv[8] = {s0[s].x, s0[s].y, s0[s].z, s0[s].w,
+                                         s1[s].x, s1[s].y, s1[s].z, s1[s].w};
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) wv[jj] *= sv[jj];
+                }
+                split3(wv, hi[f], mid[f], lo[f]);
+            }
+#pragma unroll
+            for (int f = 0; f < EF; ++f) acc[f] = rmfma(a[s], hi[f], acc[f]);
+#pragma unroll
+            for (int f = 0; f < EF; ++f) acc[f] = rmfma(a[s], mid[f], acc[f]);
+#pragma unroll
+            for (int f = 0; f < EF; ++f) acc[f] = rmfma(a[s], lo[f], acc[f]);
+        }
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int f = 0; f < EF; ++f) part[wave - 1][f][lane] = acc[f];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll 1
+    for (int w = 0; w < NW - 1; ++w) {
+#pragma unroll
+        for (int f = 0; f < EF; ++f) acc[f] += part[w][f][lane];
+    }
+#pragma unroll
+    for (int f = 0; f < EF; ++f) {
+        const float b = bias ? bias[e0 + 16 * f + l16] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 4 * g + i;
+            if (t < T) logits[(int64_t)t * E + e0 + 16 * f + l16] = acc[f][i] + b;
+        }
+    }
+}
+
 hipError_t launch_router_logits(const void* x, int x_dt, int64_t T, int H, const float* W,
                                 const float* rsc, const float* bias, int E, float* logits,
                                 hipStream_t st) {
@@ -469,11 +565,14 @@ hipError_t launch_router_logits(const void* x, int x_dt, int64_t T, int H, const
                 router_logits_mfma<4, TF, R><<<grid, 256, 0, st>>>((const uint16_t*)x, (int)T, H, W,
                                                                    rsc, bias, E, logits);
             } else if (tiles32 <= 128) {
-                // few tiles: 16 tokens per workgroup and K over 16 waves, so that
-                // each wave's chain of dependent K steps is short
-                dim3 grid((unsigned)((T + 15) / 16), E / 32);
-                router_logits_mfma<16, 1, R><<<grid, 1024, 0, st>>>((const uint16_t*)x, (int)T, H, W,
-                                                                    rsc, bias, E, logits);
+                // few tiles: 16 tokens x 16 experts per workgroup, K over 8 waves,
+                // each wave's loads issued in batches of 11 steps (all of its
+                // steps for H = 2,816; 6 with the router scale, whose loads take
+                // registers too)
+                constexpr int PF = R ? 6 : 11;
+                dim3 grid((unsigned)((T + 15) / 16), E / 16);
+                router_logits_mfma_batch<8, PF, 1, R><<<grid, 512, 0, st>>>((const uint16_t*)x, (int)T, H,
+                                                                            W, rsc, bias, E, logits);
             } else {
                 dim3 grid((unsigned)((T + 31) / 32), E / 32);
                 router_logits_mfma<4, 2, R><<<grid, 256, 0, st>>>((const uint16_t*)x, (int)T, H, W,
