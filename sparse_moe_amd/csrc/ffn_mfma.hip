@@ -61,6 +61,34 @@ MOE_DEV void stage_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Direct loads into LDS written out as instructions (16 or 4 bytes per lane;
+// lane i's bytes land at LDS address lds + size * i; M0 holds the address, with
+// the one wait state after writing it that the hardware needs).  Issued this
+// way they are invisible to the compiler's wait insertion, which tracks direct
+// loads per LDS array in a handful of slots and, past those or across the
+// ring's loop, waited for every load in flight before the reads of a stage;
+// the kernel waits for them itself (wait_vmcnt before each stage barrier).
+// They have no register results, so nothing the compiler allocates can be
+// overwritten by a load in flight.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+// buffer resource for raw, unbounded 32-bit offsets from a base address (the
+// fourth word selects 32-bit data, as untyped loads need)
+MOE_DEV i32x4 buffer_rsrc(const void* p) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    return (i32x4){(int)__builtin_amdgcn_readfirstlane((uint32_t)a),
+                   (int)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu), -1, 0x00020000};
+}
+MOE_DEV void dma16(const void* lds, uint32_t voff, i32x4 rsrc, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds)), "v"(voff), "s"(rsrc),
+                    "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory");
+}
+MOE_DEV void dma4(const void* lds, uint32_t voff, i32x4 rsrc, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds)), "v"(voff), "s"(rsrc),
+                    "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory");
+}
+
 // Position, inside a 32-element block as the MFMA reads it, of element j.
 // Lane group g holds k slots 8g..8g+7 = elements 4g, 4g+2, 4g+16, 4g+18,
 // 4g+1, 4g+3, 4g+17, 4g+19 (see dq_group).
@@ -241,18 +269,18 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
 // by (row >> 2) & 3, so the fragment reads are conflict-free), their block sums
 // [2][MT] and the tile's weight rows [NT][48 B] (a row's 36 bytes of the pair
 // as its bytes 0-15, 16-31 and 20-35: direct loads of 12 bytes would land 16
-// bytes apart, so three 16-byte loads that never cross the pair).  Each part
-// of each stage is its own LDS array and the loop runs two iterations per trip
-// with constant stage indices, so the compiler sees that the loads in flight
-// do not touch what is being read (with one array for both stages it waited
-// for every load before the reads).  The barrier is a bare s_barrier after an
-// LDS-only wait: a memory-model fence would also drain the direct loads.
+// bytes apart, so three 16-byte loads that never cross the pair).  The loads
+// are issued by dma16/dma4, so the only waits for them are the kernel's own:
+// each step waits until the next pair's loads have landed (later pairs stay in
+// flight) and ends on a bare s_barrier after an LDS-only wait (a memory-model
+// fence would also drain the direct loads).
 // Per wave and pair: MF/2 16-byte loads of activations (16 rows of one block
 // each), one 4-byte load of block sums (64 rows of one block) and three
 // 16-byte loads of weights (21 rows per instruction), in place of eight
 // per-lane weight loads that each touched 16 rows.  A third weight stage (two
 // pairs in flight) measured no faster for full tiles; tiles of at most 32
-// slots, which have a quarter of the work per pair, run a three-stage ring.
+// slots, which have a quarter of the work per pair, run a three-stage ring
+// (a fourth stage measured no faster).
 //
 // BUF: the activation buffer spans less than 2 GiB (its block sums and one
 // expert's weights are smaller still), so every offset fits a signed 32-bit
@@ -331,12 +359,8 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
         cbyte0 = (arow * cs_row + (int64_t)(wave >> 1) * cs_blk) * 4;
     }
-    // buffer resources (unbounded: every offset stays inside its buffer); the
-    // fourth descriptor word selects 32-bit data, as untyped loads need
-    constexpr int RSRC_W3 = 0x00020000;
-    const __amdgpu_buffer_rsrc_t r_act = __builtin_amdgcn_make_buffer_rsrc((void*)act, 0, -1, RSRC_W3);
-    const __amdgpu_buffer_rsrc_t r_cs = __builtin_amdgcn_make_buffer_rsrc((void*)csum, 0, -1, RSRC_W3);
-    const __amdgpu_buffer_rsrc_t r_w = __builtin_amdgcn_make_buffer_rsrc((void*)We, 0, -1, RSRC_W3);
+    // buffer resources (unbounded: every offset stays inside its buffer)
+    const i32x4 r_act = buffer_rsrc(act), r_cs = buffer_rsrc(csum), r_w = buffer_rsrc(We);
 
     const int mfa = min(8, (cnt + 15) >> 4);  // valid slot fragments
     const bool active = nfa > 0;
@@ -390,16 +414,10 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         auto issue = [&](const StageRef& S, int j) {
             if constexpr (BUF) {
 #pragma unroll
-                for (int i = 0; i < NA; ++i)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(r_act, (lds_void_t*)(S.a + adst[i]), 16,
-                                                             (int)abyte[i], 128 * j, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(r_cs, (lds_void_t*)(S.c + cdst), 4,
-                                                         (int)cbyte, cpair * j, 0, 0);
+                for (int i = 0; i < NA; ++i) dma16(S.a + adst[i], (uint32_t)abyte[i], r_act, 128u * j);
+                dma4(S.c + cdst, (uint32_t)cbyte, r_cs, (uint32_t)(cpair * j));
 #pragma unroll
-                for (int i = 0; i < 3; ++i)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        r_w, (lds_void_t*)(S.w + 64 * 48 * wave + 1024 * i), 16, (int)woff[i], 36 * j,
-                        0, 0);
+                for (int i = 0; i < 3; ++i) dma16(S.w + 64 * 48 * wave + 1024 * i, woff[i], r_w, 36u * j);
             } else {
                 const uint8_t* act_b = reinterpret_cast<const uint8_t*>(act);
                 const uint8_t* cs_b = reinterpret_cast<const uint8_t*>(csum);
