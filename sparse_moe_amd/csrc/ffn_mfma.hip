@@ -26,6 +26,7 @@
 // a wave's 64 rows are 32 gate rows and the 32 up rows of the same hidden
 // columns, so each lane holds gate and up of the same (slot, column) in
 // matching registers and GELU(g) * u is formed in the epilogue.
+#include <algorithm>
 #include <type_traits>
 
 #include "kernels.h"
@@ -116,29 +117,33 @@ MOE_DEV f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 // Tile lookup.  Slot tiles cover an expert's slots MT at a time (the last one
-// partial); each slot tile has n_tiles column tiles.  The grid is an upper
-// bound on the tile count, so the numbering is made once the real count is
-// known; the column tiles of one slot tile always take consecutive block
+// partial); each has n_tiles column tiles.
+// The grid is an upper bound, so the numbering is made once the real counts
+// are known; the column tiles of one slot tile always take consecutive block
 // numbers of one XCD (blocks congruent to x mod 8 run on XCD x), so they share
 // that XCD's L2.
 //
-//  * Many tiles (more than FFN_MFMA_LPT_UNITS workgroups): slot tiles in
-//    expert order, the sequence cut into 8 equal runs of consecutive numbers,
-//    run x for XCD x, so the next slot tile of the same expert also shares the
-//    XCD's L2 (its weights).
-//  * Few tiles (a grid of about three rounds of resident workgroups or less, as
-//    with a few hundred tokens over many experts): how long the kernel takes
-//    is decided by how the tiles pack, and a tile's time grows with its slot
-//    count.  The slot tiles are ranked longest first (tiles of 97-128 slots,
-//    then 65-96, 33-64 and 1-32; expert order within a class) and rank r goes
-//    to XCD r mod 8, so every XCD starts its long tiles first and the short
-//    ones fill in behind them.
+//  * Many workgroups (more than FFN_MFMA_LPT_UNITS): slot tiles in expert
+//    order, the sequence of workgroups cut into 8 equal runs, run x for XCD
+//    x, so the next slot tile of the same expert also shares the XCD's L2 (its
+//    weights).
+//  * Few (a grid of about three rounds of resident workgroups or less, as with
+//    a few hundred tokens over many experts): how long the kernel takes is
+//    decided by how the tiles pack, and a tile's time grows with its slot
+//    count.  Slot tiles are ranked longest first (97-128 slots, then 65-96,
+//    33-64, 1-32; expert order within a class) and rank r goes to XCD r mod 8,
+//    so every XCD starts its long tiles first and the short ones fill in.
+//    A light slot tile (at most 32 slots) here has 2 n_tiles half-width
+//    column tiles: it streams the same weight bytes as a full tile for a
+//    quarter of the products, so it runs almost as long, and halving its
+//    columns halves the granule that the last round packs.
 //
 // Wave 0 scans the expert counts (up to 4 experts per lane); returns false
-// for a workgroup without a tile.
+// for a workgroup without a tile.  half: ntile counts half-width column tiles.
 constexpr int FFN_MFMA_LPT_UNITS = 1536;
+constexpr int FFN_MFMA_LIGHT = 32;  // slot tiles of at most this many slots are light
 
-MOE_DEV int tile_class(int size) { return size > 96 ? 0 : size > 64 ? 1 : size > 32 ? 2 : 3; }
+MOE_DEV int tile_class(int size) { return size > 96 ? 0 : size > 64 ? 1 : size > FFN_MFMA_LIGHT ? 2 : 3; }
 
 MOE_DEV int scan_incl(int v, int lane) {
 #pragma unroll
@@ -149,38 +154,40 @@ MOE_DEV int scan_incl(int v, int lane) {
     return v;
 }
 
-__device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
-                          int n_tiles, int* s_res, int& e_out, int& base, int& cnt, int& ntile) {
+__device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid, int n_tiles, int* s_res,
+                          int& e_out, int& base, int& cnt, int& ntile, bool& half) {
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
-        int c[4], t[4], tot = 0;
+        int c[4], full[4], rem[4], u[4], tot = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int e = lane * 4 + q;
             c[q] = e < E ? offsets[e + 1] - offsets[e] : 0;
-            t[q] = (c[q] + MT - 1) / MT;
-            tot += t[q];
+            full[q] = c[q] / MT;
+            rem[q] = c[q] - full[q] * MT;
+            u[q] = (full[q] + (rem[q] ? 1 : 0)) * n_tiles;  // column tiles
+            tot += u[q];
         }
         const int incl = scan_incl(tot, lane);
-        const int R = __shfl(incl, 63);  // slot tiles
-        const int total = R * n_tiles;
+        const int total = __shfl(incl, 63);  // workgroups with a tile
         // this lane's find: expert, its slot tile, column tile
         int e_sel = -1, k_sel = 0, c_sel = 0, nt_sel = 0;
-        if (total > FFN_MFMA_LPT_UNITS) {
+        const bool many = total > FFN_MFMA_LPT_UNITS;
+        if (many) {
             const int per_xcd = (total + 7) >> 3;
             const int lin = (bid & 7) * per_xcd + (bid >> 3);
             const bool have = (bid >> 3) < per_xcd && lin < total;
-            const int tile = have ? lin / n_tiles : -1;
             int run = incl - tot;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                if (tile >= run && tile < run + t[q]) {
+                if (have && lin >= run && lin < run + u[q]) {
+                    const int ue = lin - run;
                     e_sel = lane * 4 + q;
-                    k_sel = tile - run;
                     c_sel = c[q];
-                    nt_sel = lin - tile * n_tiles;
+                    k_sel = ue / n_tiles;
+                    nt_sel = ue - k_sel * n_tiles;
                 }
-                run += t[q];
+                run += u[q];
             }
         } else {
             // tiles per class: class 0 holds an expert's full tiles and a
@@ -188,8 +195,8 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
             int n0[4], rc[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int rem = c[q] % MT, cls = rem ? tile_class(rem) : -1;
-                n0[q] = c[q] / MT + (cls == 0 ? 1 : 0);
+                const int cls = rem[q] ? tile_class(rem[q]) : -1;
+                n0[q] = full[q] + (cls == 0 ? 1 : 0);
                 rc[q] = cls > 0 ? cls : -1;
             }
             auto lane_count = [&](int k) {
@@ -199,16 +206,29 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
                 return s;
             };
             // inclusive scans of the class counts, two 16-bit fields per int (in
-            // this branch a class holds at most R <= FFN_MFMA_LPT_UNITS tiles)
+            // this branch a class holds at most FFN_MFMA_LPT_UNITS tiles)
             const int s01 = scan_incl(lane_count(0) + (lane_count(1) << 16), lane);
             const int s23 = scan_incl(lane_count(2) + (lane_count(3) << 16), lane);
             const int a01 = __shfl(s01, 63), a23 = __shfl(s23, 63);
-            const int tot0 = a01 & 0xFFFF, tot1 = a01 >> 16, tot2 = a23 & 0xFFFF;
+            const int tot0 = a01 & 0xFFFF, tot1 = a01 >> 16, tot2 = a23 & 0xFFFF, tot3 = a23 >> 16;
+            const int R = tot0 + tot1 + tot2 + tot3, T012 = tot0 + tot1 + tot2;
+            // XCD x takes ranks x, x + 8, ...: its first c012 of them are of
+            // classes 0-2 (n_tiles units each), the rest light (2 n_tiles)
             const int x = bid & 7, qpos = bid >> 3;
-            const int s8 = qpos / n_tiles;
-            const int r = s8 * 8 + x;  // rank of this block's slot tile
+            const int c012 = T012 > x ? (T012 - x + 7) >> 3 : 0;
+            int i, nt;
+            if (qpos < c012 * n_tiles) {
+                i = qpos / n_tiles;
+                nt = qpos - i * n_tiles;
+            } else {
+                const int q2 = qpos - c012 * n_tiles;
+                const int j = q2 / (2 * n_tiles);
+                i = c012 + j;
+                nt = q2 - j * 2 * n_tiles;
+            }
+            const int r = x + 8 * i;  // rank of this block's slot tile
             if (r < R) {
-                const int k = r < tot0 ? 0 : r < tot0 + tot1 ? 1 : r < tot0 + tot1 + tot2 ? 2 : 3;
+                const int k = r < tot0 ? 0 : r < tot0 + tot1 ? 1 : r < T012 ? 2 : 3;
                 const int idx = r - (k >= 1 ? tot0 : 0) - (k >= 2 ? tot1 : 0) - (k >= 3 ? tot2 : 0);
                 const int inclk = k == 0 ? (s01 & 0xFFFF) : k == 1 ? (s01 >> 16)
                                 : k == 2 ? (s23 & 0xFFFF) : (s23 >> 16);
@@ -218,9 +238,10 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
                     const int nq = k == 0 ? n0[q] : (rc[q] == k ? 1 : 0);
                     if (idx >= run && idx < run + nq) {
                         e_sel = lane * 4 + q;
-                        k_sel = k == 0 ? idx - run : c[q] / MT;
+                        // class 0: the (idx - run)-th tile of the expert; others: its remainder
+                        k_sel = k == 0 ? idx - run : full[q];
                         c_sel = c[q];
-                        nt_sel = qpos - s8 * n_tiles;
+                        nt_sel = nt;
                     }
                     run += nq;
                 }
@@ -231,6 +252,7 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
             s_res[1] = offsets[e_sel] + k_sel * MT;
             s_res[2] = min(MT, c_sel - k_sel * MT);
             s_res[3] = nt_sel;
+            s_res[4] = !many && c_sel - k_sel * MT <= FFN_MFMA_LIGHT;
         }
         // exactly one lane finds the tile; without one lane 63 marks the block
         // (the whole wave votes)
@@ -242,6 +264,7 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid,
     base = s_res[1];
     cnt = s_res[2];
     ntile = s_res[3];
+    half = s_res[4] != 0;
     return e_out >= 0;
 }
 
@@ -309,10 +332,11 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         uint8_t* w;
     };
     StageRef st0{a0, cc0, w0}, st1{a1, cc1, w1};
-    __shared__ int s_res[4];
+    __shared__ int s_res[5];
 
     int e, base, cnt, ntile;
-    if (!find_tile(offsets, E, blockIdx.x, n_tiles, s_res, e, base, cnt, ntile)) return;
+    bool half;
+    if (!find_tile(offsets, E, blockIdx.x, n_tiles, s_res, e, base, cnt, ntile, half)) return;
     e = __builtin_amdgcn_readfirstlane(e);
     base = __builtin_amdgcn_readfirstlane(base);
     cnt = __builtin_amdgcn_readfirstlane(cnt);
@@ -325,32 +349,6 @@ __global__ __launch_bounds__(256) void ffn_mfma(
     const uint8_t* We = W + (size_t)e * rows_e * rowbytes;
     const int npairs = nb >> 1;
 
-    // ---- this wave's weight rows ----
-    // MODE 0: hidden columns c0 .. c0+31 (rows of gate, then the same rows of up)
-    // MODE 1: output rows c0 .. c0+63
-    const int c0 = MODE == 0 ? ntile * (NT / 2) + 32 * wave : ntile * NT + 64 * wave;
-    int nfa;  // valid row fragments (whole wave for MODE 0)
-    if (MODE == 0)
-        nfa = c0 < ncols ? 4 : 0;
-    else
-        nfa = max(0, min(4, (ncols - c0) >> 4));
-    // weight pieces: a row's 36 bytes of a pair as three 16-byte loads of its
-    // bytes 0-15, 16-31 and 20-35 (never past the pair), 48 bytes per row in
-    // LDS; lane piece i of a pair is q = 64 i + lane of the wave's 192 pieces,
-    // row 16 nf + l16 = q / 3 of the wave, piece q % 3
-    uint32_t woff[3];
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-        const int q = 64 * i + lane, r = q / 3;
-        const int nf = r >> 4, rl = r & 15;
-        int row;
-        if (MODE == 0)
-            row = min(c0 + (nf & 1) * 16 + rl, ncols - 1) + (nf >> 1) * ncols;
-        else
-            row = min(c0 + nf * 16 + rl, rows_e - 1);
-        const int pc = q % 3;
-        woff[i] = (uint32_t)row * rowbytes + (pc == 0 ? 0u : pc == 1 ? 16u : 20u);
-    }
     // block sums: wave w loads block w >> 1 of tile rows 64 (w & 1) + lane
     int64_t cbyte0;  // byte offset in csum
     {
@@ -363,22 +361,56 @@ __global__ __launch_bounds__(256) void ffn_mfma(
     const i32x4 r_act = buffer_rsrc(act), r_cs = buffer_rsrc(csum), r_w = buffer_rsrc(We);
 
     const int mfa = min(8, (cnt + 15) >> 4);  // valid slot fragments
-    const bool active = nfa > 0;
 
     // The main loop and epilogue for MF slot fragments (16 slots each).  A tile
     // of at most 32, 64 or 96 slots (an expert's last, partial tile, or a small
     // expert) runs with MF = 2, 4 or 6: a quarter, half or three quarters of
     // the activation loads, MFMAs and scale FMAs of a full tile.
-    auto run = [&](auto mf_const) {
+    auto run = [&](auto mf_const, auto nf_const) {
         constexpr int MF = decltype(mf_const)::value;
         constexpr int NA = MF / 2;  // activation loads per wave per pair
         constexpr bool LIGHT = MF == 2;
         constexpr int AROWS = LIGHT ? 32 : MT;  // rows per block in a stage
-        f32x4 acc[MF][4];
+        // 16-row weight fragments per wave: 4, or 2 in a light tile's
+        // half-width column tiles
+        constexpr int NF = decltype(nf_const)::value;
+        constexpr int NWL = (48 * NF + 63) / 64;  // 16-byte weight loads per wave per pair
+
+        // ---- this wave's weight rows ----
+        // MODE 0: hidden columns c0 .. c0 + 8 NF - 1 (gate rows, then the same
+        //         rows of up)
+        // MODE 1: output rows c0 .. c0 + 16 NF - 1
+        const int c0 = MODE == 0 ? ntile * (32 * NF) + 8 * NF * wave : ntile * (64 * NF) + 16 * NF * wave;
+        int nfa;  // valid row fragments (whole wave for MODE 0)
+        if (MODE == 0)
+            nfa = c0 < ncols ? NF : 0;
+        else
+            nfa = max(0, min(NF, (ncols - c0) >> 4));
+        const bool active = nfa > 0;
+        // weight pieces: a row's 36 bytes of a pair as three 16-byte loads of its
+        // bytes 0-15, 16-31 and 20-35 (never past the pair), 48 bytes per row in
+        // LDS; lane piece i of a pair is q = 64 i + lane of the wave's 48 NF
+        // pieces (lanes past them repeat the last one), row 16 nf + l16 = q / 3
+        // of the wave, piece q % 3
+        uint32_t woff[NWL];
+#pragma unroll
+        for (int i = 0; i < NWL; ++i) {
+            const int q = min(64 * i + lane, 48 * NF - 1), r = q / 3;
+            const int nf = r >> 4, rl = r & 15;
+            int row;
+            if (MODE == 0)
+                row = min(c0 + (nf % (NF / 2)) * 16 + rl, ncols - 1) + (nf / (NF / 2)) * ncols;
+            else
+                row = min(c0 + nf * 16 + rl, rows_e - 1);
+            const int pc = q % 3;
+            woff[i] = (uint32_t)row * rowbytes + (pc == 0 ? 0u : pc == 1 ? 16u : 20u);
+        }
+
+        f32x4 acc[MF][NF];
 #pragma unroll
         for (int i = 0; i < MF; ++i)
 #pragma unroll
-            for (int jn = 0; jn < 4; ++jn) acc[i][jn] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            for (int jn = 0; jn < NF; ++jn) acc[i][jn] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
         // activation loads: the WG's 2 MF instructions t = NA w + i cover block
         // t / MF, rows 16 (t % MF) .. +15; lane: row + (lane >> 2), LDS chunk
@@ -417,7 +449,7 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                 for (int i = 0; i < NA; ++i) dma16(S.a + adst[i], (uint32_t)abyte[i], r_act, 128u * j);
                 dma4(S.c + cdst, (uint32_t)cbyte, r_cs, (uint32_t)(cpair * j));
 #pragma unroll
-                for (int i = 0; i < 3; ++i) dma16(S.w + 64 * 48 * wave + 1024 * i, woff[i], r_w, 36u * j);
+                for (int i = 0; i < NWL; ++i) dma16(S.w + 64 * 48 * wave + 1024 * i, woff[i], r_w, 36u * j);
             } else {
                 const uint8_t* act_b = reinterpret_cast<const uint8_t*>(act);
                 const uint8_t* cs_b = reinterpret_cast<const uint8_t*>(csum);
@@ -428,7 +460,7 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                 __builtin_amdgcn_global_load_lds((glb_void_t*)(cs_b + cbyte + (int64_t)cpair * j),
                                                  (lds_void_t*)(S.c + cdst), 4, 0, 0);
 #pragma unroll
-                for (int i = 0; i < 3; ++i)
+                for (int i = 0; i < NWL; ++i)
                     __builtin_amdgcn_global_load_lds(
                         (glb_void_t*)(We + woff[i] + 36u * (uint32_t)j),
                         (lds_void_t*)(S.w + 64 * 48 * wave + 1024 * i), 16, 0, 0);
@@ -447,10 +479,10 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                 // this block's weights: the scale and the lane's qs dword (block 0:
                 // bytes 2 + 4g .. 5 + 4g of the pair, two dwords and an alignbyte;
                 // block 1: bytes 20 + 4g .. 23 + 4g)
-                float dv[4];
-                u32x4 bq[4];
+                float dv[NF];
+                u32x4 bq[NF];
 #pragma unroll
-                for (int nf = 0; nf < 4; ++nf) {
+                for (int nf = 0; nf < NF; ++nf) {
                     const uint8_t* rp = WL + nf * 16 * 48;
                     if (blk == 0) {
                         const uint32_t lo = *(const uint32_t*)(rp + 4 * g);
@@ -474,11 +506,11 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                     const u32x4 a =
                         *(const u32x4*)(S.a + blk * AROWS * 64 + (mf * 16 + l16) * 64 + swz);
                     const f32x4 c = *(const f32x4*)&S.c[blk * AROWS + mf * 16 + 4 * g];
-                    f32x4 t[4];
+                    f32x4 t[NF];
 #pragma unroll
-                    for (int nf = 0; nf < 4; ++nf) t[nf] = mfma_bf16(a, bq[nf], c);
+                    for (int nf = 0; nf < NF; ++nf) t[nf] = mfma_bf16(a, bq[nf], c);
 #pragma unroll
-                    for (int nf = 0; nf < 4; ++nf)
+                    for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) acc[mf][nf][i] = fmaf(dv[nf], t[nf][i], acc[mf][nf][i]);
                 }
@@ -492,7 +524,7 @@ __global__ __launch_bounds__(256) void ffn_mfma(
             // j+2 into the stage pair j-1 used and waits for pair j+1 (issued a
             // step earlier)
             const StageRef st2{la2, lc2, w2};
-            constexpr int OPS = NA + 4;  // direct loads per wave per pair
+            constexpr int OPS = NA + 1 + NWL;  // direct loads per wave per pair
             auto step = [&](const StageRef& cur, const StageRef& nxt, int j) {
                 const bool more = j + 2 < npairs;
                 if (more) issue(nxt, j + 2);
@@ -536,7 +568,56 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         // The last step issues nothing, waits for all of its wave's loads and
         // ends on the barrier: the stage arrays are free for the epilogues.
         if (!active) return;
-        if (MODE == 0) {
+        if constexpr (MODE == 0 && NF == 2) {
+            // A light tile's half-width column tile: waves 2k and 2k+1 hold
+            // columns 0-15 and 16-31 of h block c0 >> 5.  Each writes its h values
+            // into the pair's staging rows and its 16-column row sums to LDS; after
+            // a barrier the even wave adds the two halves (columns 0-15 first) and
+            // stores the rows.  The four waves are active together or not at all
+            // (I is a multiple of 64, the width of the tile), so all reach the
+            // barrier.
+            const int hblk = c0 >> 5, half = wave & 1;
+            constexpr int RB = 80;
+            static_assert(32 * RB <= 2 * MT * 64 && 4 * 32 * 4 <= NT * 48, "light h staging fits");
+            uint8_t* R = (wave >> 1) ? a1 : a0;
+            float* psum = reinterpret_cast<float*>(w0);  // [wave][row]
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf) {
+                if (mf < mfa) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = mf * 16 + 4 * g + i;
+                        const float gv = 16.f * acc[mf][0][i], uv = 16.f * acc[mf][1][i];
+                        const uint16_t hb = f32_to_bf16(gelu_tanh(gv) * uv);
+                        float s = bf16_to_f32(hb);
+                        *(uint16_t*)(R + r * RB + 2 * perm_pos(half * 16 + l16)) = hb;
+                        s += dpp_mov_f32<DPP_QUAD_XOR1>(s);
+                        s += dpp_mov_f32<DPP_QUAD_XOR2>(s);
+                        s += dpp_mov_f32<DPP_ROW_HALF_MIRROR>(s);
+                        s += dpp_mov_f32<DPP_ROW_MIRROR>(s);
+                        if (l16 == 0) psum[wave * 32 + r] = s;
+                    }
+                }
+            }
+            __syncthreads();
+            if (half == 0) {
+#pragma unroll
+                for (int mf = 0; mf < MF; ++mf) {
+                    if (mf < mfa) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = mf * 16 + 4 * g + i;
+                            if (r < cnt && l16 == 0)
+                                hsum_out[(int64_t)hblk * hs_blk + base + r] =
+                                    -1.5f * (psum[wave * 32 + r] + psum[(wave + 1) * 32 + r]);
+                        }
+                        const int r = mf * 16 + (lane >> 2), ch = lane & 3;
+                        const uint4 v = *(const uint4*)(R + r * RB + 16 * ch);
+                        if (r < cnt) *(uint4*)(h_out + (int64_t)(base + r) * hpitch + hblk * 32 + 8 * ch) = v;
+                    }
+                }
+            }
+        } else if constexpr (MODE == 0) {
             // h = GELU(g) * u for hidden columns c0 .. c0+31: one Q4_0 block of the
             // down product's K, written in the MFMA order with its sum.  Each slot
             // fragment's 16 rows of 64 bytes go through a stage array of the wave's
@@ -592,7 +673,7 @@ __global__ __launch_bounds__(256) void ffn_mfma(
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
 #pragma unroll
-                        for (int nf = 0; nf < 4; ++nf)
+                        for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
                                 R[(16 * h + 4 * g + i) * RS + 16 * nf + l16] = 16.f * acc[m2 + h][nf][i];
@@ -607,14 +688,20 @@ __global__ __launch_bounds__(256) void ffn_mfma(
             }
         }
     };
-    if (cnt <= 32)
-        run(std::integral_constant<int, 2>{});
-    else if (cnt <= 64)
-        run(std::integral_constant<int, 4>{});
-    else if (cnt <= 96)
-        run(std::integral_constant<int, 6>{});
-    else
-        run(std::integral_constant<int, 8>{});
+    using F2 = std::integral_constant<int, 2>;
+    using F4 = std::integral_constant<int, 4>;
+    if (cnt <= 32) {
+        if (half)
+            run(std::integral_constant<int, 2>{}, F2{});
+        else
+            run(std::integral_constant<int, 2>{}, F4{});
+    } else if (cnt <= 64) {
+        run(std::integral_constant<int, 4>{}, F4{});
+    } else if (cnt <= 96) {
+        run(std::integral_constant<int, 6>{}, F4{});
+    } else {
+        run(std::integral_constant<int, 8>{}, F4{});
+    }
 }
 
 // Activations -> MFMA block order (rows pitch apart), plus -1.5 * block sums
@@ -666,6 +753,17 @@ __global__ __launch_bounds__(256) void ffn_mfma_prep(const uint16_t* __restrict_
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
+// Grid of a grouped-GEMM launch over at most mtiles slot tiles: room for
+// ceil(mtiles / 8) slot tiles per XCD with all their column tiles, and, when
+// the longest-first numbering is possible (at most FFN_MFMA_LPT_UNITS column
+// tiles in all), for its half-width light column tiles.
+static int mfma_grid(int mtiles, int n_tiles) {
+    const int g_many = (mtiles + 7) / 8 * 8 * n_tiles;
+    const int r_few = std::min(mtiles, FFN_MFMA_LPT_UNITS / n_tiles);
+    const int g_few = (r_few + 7) / 8 * 8 * 2 * n_tiles;
+    return std::max(g_many, g_few);
+}
+
 }  // namespace
 
 // Row pitch (elements) of a staged activation matrix with `cols` bf16 columns
@@ -705,11 +803,9 @@ hipError_t launch_ffn_mfma(const void* x, int64_t T, int H, const uint8_t* w_gat
     // slot tiles: sum over experts of ceil(count / MT) <= N / MT + (experts hit);
     // the workgroups past the real count exit at once
     const int mtiles = N / MT + min(E, N);
-    // grid: room for ceil(mtiles / 8) slot tiles per XCD with all their column
-    // tiles (either numbering fits in it)
     {
         const int n_tiles = (I + NT / 2 - 1) / (NT / 2);
-        const int total = (mtiles + 7) / 8 * 8 * n_tiles;
+        const int total = mfma_grid(mtiles, n_tiles);
         if (buf_ok((size_t)T * xpitch * 2))
             ffn_mfma<0, true><<<total, 256, 0, st>>>(xp, xs, w_gate_up, H / 32, xpitch, 2 * I, I, H / 32, 1,
                                                      hpitch, N, n_tiles, offsets, sorted_slots, K, E, hp,
@@ -721,7 +817,7 @@ hipError_t launch_ffn_mfma(const void* x, int64_t T, int H, const uint8_t* w_gat
     }
     {
         const int n_tiles = (H + NT - 1) / NT;
-        const int total = (mtiles + 7) / 8 * 8 * n_tiles;
+        const int total = mfma_grid(mtiles, n_tiles);
         if (buf_ok((size_t)N * hpitch * 2))
             ffn_mfma<1, true><<<total, 256, 0, st>>>(hp, hs, w_down, I / 32, hpitch, H, H, 1, N, 0, 0,
                                                      n_tiles, offsets, sorted_slots, K, E, nullptr, nullptr,
@@ -749,7 +845,7 @@ hipError_t launch_linear_mfma(const void* x, int64_t T, int H, const uint8_t* W,
                                                                       xp, xs);
     const int N = (int)T, mtiles = N / MT + 1;
     const int n_tiles = (R + NT - 1) / NT;
-    const int total = (mtiles + 7) / 8 * 8 * n_tiles;
+    const int total = mfma_grid(mtiles, n_tiles);
     if (buf_ok((size_t)T * xpitch * 2))
         ffn_mfma<1, true><<<total, 256, 0, st>>>(xp, xs, W, H / 32, xpitch, R, R, H / 32, 1, 0, 0,
                                                  n_tiles, offsets, slots, 1, 1, nullptr, nullptr, y);
