@@ -224,7 +224,7 @@ moe_status moe_layer_decode(const void* x, int x_dt, int64_t T, int32_t H, const
  * looked up once per device (hipGetSymbolAddress) and kept.
  *  - Returns MOE_ERR_SCRATCH, enqueueing nothing, when
  *    moe_expert_ffn_q4_0_workspace_bytes(T, K, H, I, E, x_dt) exceeds the
- *    array (at the Gemma shape: about 934 tokens on the bf16 MFMA path; every
+ *    array (at the Gemma shape: about 927 tokens on the bf16 MFMA path; every
  *    decode batch of fewer than 64 tokens fits).
  *  - Every call on one GPU shares that GPU's array, and the array keeps the
  *    last call's contents (the workspace needs no initialisation).  Calls
