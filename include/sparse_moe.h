@@ -189,14 +189,24 @@ moe_status moe_expert_ffn_q4_0(const void* x, int x_dt, int64_t T, int32_t H,
  * logits; gate/up with top-K and the permutation computed inside every
  * workgroup (no hand-off through a completion counter); down with the
  * weighted combine inside (each workgroup owns a few output rows of one token
- * and sums its K experts there, so no per-slot output y is stored).
+ * and sums its K experts there, so no per-slot output y is stored).  One
+ * token at 2048 < H <= 4096, 512 < I <= 1024 and K <= 8 (the Gemma shape)
+ * runs gate/up and down in ONE launch: the down workgroups fetch their
+ * weights, then wait on completion counters bumped by the gate/up workgroups
+ * (a bounded wait; see ws below).
  *
  *   Arguments are those of the three calls: W_r == NULL selects injected
  *   logits (then `logits` is an INPUT); logits, topk_ids, topk_w,
  *   expert_offsets, sorted_slots and slot_pos are OUTPUTS as there (required);
  *   out_f32 / out_act / residual as in moe_combine (at least one output).
- *   ws   >= moe_layer_decode_workspace_bytes(T, K, H, I, E, x_dt) bytes (the
- *        hidden h); contents need no initialisation.
+ *   ws   >= moe_layer_decode_workspace_bytes(T, K, H, I, E, x_dt) bytes,
+ *        16-byte aligned: a 16 KiB header of completion counters (zeroed by
+ *        the call itself), then the hidden h; contents need no
+ *        initialisation.  After the call, int 1 of ws is non-zero only if the
+ *        one-launch path's bounded wait expired (then the output is not
+ *        written); it never does while the launch runs alone on the GPU's
+ *        queue, since every waiting workgroup was dispatched after the
+ *        workgroups it waits for.
  * Supported shapes: 1 <= T <= 8, T * K <= 64, H and I multiples of 64, and
  * K * (I / 32) * 68 bytes of staged hidden digits <= 64 KiB; other shapes
  * return MOE_ERR_UNSUPPORTED (use the separate calls).  The hidden h goes

@@ -212,8 +212,10 @@ size_t moe_layer_decode_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_t
     if (check_ekh(T, K, E) != MOE_OK || check_dim(H, MOE_MAX_H) != MOE_OK ||
         check_dim(I, MOE_MAX_I) != MOE_OK || !dtype_ok(x_dt))
         return 0;
-    // the hidden h [T*K, I] in the activation dtype, in sorted-slot order
-    return round_up((size_t)(T * K) * (size_t)I * (x_dt == MOE_F32 ? 4 : 2), 256);
+    // [0, DECODE_CTR_BYTES): the one-token path's completion counters and
+    // timeout flag; then the hidden h [T*K, I] in the activation dtype, in
+    // sorted-slot order
+    return moe::DECODE_CTR_BYTES + round_up((size_t)(T * K) * (size_t)I * (x_dt == MOE_F32 ? 4 : 2), 256);
 }
 
 moe_status moe_layer_decode(const void* x, int x_dt, int64_t T, int32_t H, const float* W_r,
@@ -246,13 +248,18 @@ moe_status moe_layer_decode(const void* x, int x_dt, int64_t T, int32_t H, const
     if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
     if (!aligned16(ws)) return MOE_ERR_ALIGN;
     hipStream_t st = (hipStream_t)stream;
-    if (W_r && (s = hip_status(moe::launch_router_logits(x, x_dt, T, H, W_r, r_scale, logit_bias, E,
-                                                        logits, st))) != MOE_OK)
+    int* ctr = (int*)ws;  // zeroed by this call's router launch (or a launch of its own)
+    if (W_r) {
+        if ((s = hip_status(moe::launch_router_logits(x, x_dt, T, H, W_r, r_scale, logit_bias, E,
+                                                      logits, st, ctr))) != MOE_OK)
+            return s;
+    } else if ((s = hip_status(moe::launch_zero_decode_ctr(ctr, st))) != MOE_OK) {
         return s;
+    }
     return hip_status(moe::launch_decode_layer(
         x, x_dt, (int)T, H, logits, E, K, (const uint8_t*)w_gate_up, (const uint8_t*)w_down, I,
         expert_scale, topk_ids, topk_w, expert_offsets, sorted_slots, slot_pos, residual,
-        residual_dt, out_f32, out_act, out_dt, ws, st));
+        residual_dt, out_f32, out_act, out_dt, (uint8_t*)ws + moe::DECODE_CTR_BYTES, ctr, st));
 }
 
 moe_status moe_expert_ffn_q4_0_noalloc(const void* x, int x_dt, int64_t T, int32_t H,

@@ -50,6 +50,17 @@ MOE_DEV void coherent_store(float* p, float v) {
 MOE_DEV float coherent_load(const float* p) {
     return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+MOE_DEV void coherent_store_act(void* p, int dt, int64_t i, float v) {
+    if (dt == MOE_F32)
+        coherent_store((float*)p + i, v);
+    else
+        __hip_atomic_store((uint16_t*)p + i, (uint16_t)f32_to_bf16(v), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+MOE_DEV uint64_t coherent_load_u64(const void* p) {
+    return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // ---- workgroup barrier ordering LDS only ------------------------------------------
 // __syncthreads() fences all memory, which makes the compiler drain every

@@ -25,6 +25,7 @@
 // activation digits stay in registers; a row is covered by LPR lanes (a power
 // of two >= blocks/2), a wave covers 64/LPR rows per step, and the loads of a
 // wave are contiguous.
+#include <algorithm>
 #include <type_traits>
 
 #include "route_dev.h"
@@ -41,9 +42,32 @@ namespace moe {
 // lane m of the quad owns elements 4m..4m+3 and 4m+16..4m+19, so it produces
 // the 4 words of qs dword m; the block maximum comes from a quad reduction.
 // Every lane of a quad must be active.
-template <int ADT>
+// COH: agent-scope relaxed 8-byte loads, for data another workgroup of the
+// same launch stored with agent-scope stores (coherent across the L2 slices)
+template <int ADT, bool COH = false>
 MOE_DEV void load_quarter(const void* src, int64_t e0, int m, float v[8]) {
-    if (ADT == MOE_F32) {
+    if (COH) {
+        uint64_t u[4];
+        if (ADT == MOE_F32) {
+            const float* f = (const float*)src + e0 + 4 * m;
+            u[0] = coherent_load_u64(f); u[1] = coherent_load_u64(f + 2);
+            u[2] = coherent_load_u64(f + 16); u[3] = coherent_load_u64(f + 18);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[2 * j] = __uint_as_float((uint32_t)u[j]);
+                v[2 * j + 1] = __uint_as_float((uint32_t)(u[j] >> 32));
+            }
+        } else {
+            const uint16_t* s = (const uint16_t*)src + e0 + 4 * m;
+            u[0] = coherent_load_u64(s); u[1] = coherent_load_u64(s + 16);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const uint32_t lo = (uint32_t)u[j], hi = (uint32_t)(u[j] >> 32);
+                v[4 * j] = __uint_as_float(lo << 16); v[4 * j + 1] = __uint_as_float(lo & 0xFFFF0000u);
+                v[4 * j + 2] = __uint_as_float(hi << 16); v[4 * j + 3] = __uint_as_float(hi & 0xFFFF0000u);
+            }
+        }
+    } else if (ADT == MOE_F32) {
         const float4 lo = reinterpret_cast<const float4*>((const float*)src + e0 + 4 * m)[0];
         const float4 hi = reinterpret_cast<const float4*>((const float*)src + e0 + 16 + 4 * m)[0];
         v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
@@ -246,7 +270,7 @@ struct NoRoute {
 };
 
 template <int MODE, int ADT, int LPR, int TC, int UPW, bool EVEN_NB, bool DIRECT, bool ONE,
-          bool SLOT_H = false, class Route = NoRoute>
+          bool SLOT_H = false, bool COH = false, class Route = NoRoute>
 MOE_DEV void gemv_tile(const uint8_t* __restrict__ W, int nb, int I, int H,
                        const void* __restrict__ act, const int32_t* offsets,
                        const int32_t* sorted_slots, int K, int E,
@@ -464,8 +488,9 @@ MOE_DEV void gemv_tile(const uint8_t* __restrict__ W, int nb, int I, int H,
                 const int64_t p = p0 + c0 + t;
                 const int row = row0 + u;
                 if (MODE == 0)
-                    store_act(out, ADT, (SLOT_H ? (int64_t)sorted_slots[p] : p) * I + row,
-                              gelu_tanh(mine[0]) * mine[NR - 1]);
+                    (COH ? coherent_store_act : store_act)(
+                        out, ADT, (SLOT_H ? (int64_t)sorted_slots[p] : p) * I + row,
+                        gelu_tanh(mine[0]) * mine[NR - 1]);
                 else
                     reinterpret_cast<float*>(out)[p * H + row] = mine[0];
             }
@@ -479,8 +504,9 @@ MOE_DEV void gemv_tile(const uint8_t* __restrict__ W, int nb, int I, int H,
                         const int64_t p = p0 + c0 + t;
                         const int row = row0 + lr;
                         if (MODE == 0)
-                            store_act(out, ADT, (SLOT_H ? (int64_t)sorted_slots[p] : p) * I + row,
-                                      gelu_tanh(res[u][t][0]) * res[u][t][NR - 1]);
+                            (COH ? coherent_store_act : store_act)(
+                                out, ADT, (SLOT_H ? (int64_t)sorted_slots[p] : p) * I + row,
+                                gelu_tanh(res[u][t][0]) * res[u][t][NR - 1]);
                         else
                             reinterpret_cast<float*>(out)[p * H + row] = res[u][t][0];
                     }
@@ -678,33 +704,32 @@ __global__ __launch_bounds__(256) void decode_gate_up(
 // down GEMV's lane layout and arithmetic (a unit = one expert's row, LPR lanes,
 // each lane a block pair in registers), and sums them in the combine's fixed
 // k order with the routing weight times the expert scale, adding the
-// residual for the activation-type output.
-template <int ADT, int LPR, int KB, int RR>
-__global__ __launch_bounds__(256) void decode_down_combine(
-    const uint8_t* __restrict__ Wd, int nb, int H, const void* __restrict__ hbuf,
-    const int32_t* __restrict__ ids, const float* __restrict__ tw,
-    const float* __restrict__ scale, int K,
-    const void* __restrict__ residual, int rdt, float* __restrict__ out_f32,
-    void* __restrict__ out_act, int odt) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+// residual for the activation-type output.  ids_t / w_t: the token's K expert
+// ids and routing weights (global memory, or LDS in the one-launch decode).
+// The weight windows and combine factors are loaded first; wait() then
+// returns whether the hidden rows may be read (the one-launch decode waits
+// there for the gate/up workgroups), and only then are they loaded.
+template <int ADT, int LPR, int KB, int RR, bool COH = false, class Wait>
+MOE_DEV void down_combine_tile(const uint8_t* __restrict__ Wd, int nb, int H, const void* __restrict__ hbuf,
+                               const int32_t* ids_t, const float* w_t, const float* __restrict__ scale,
+                               int K, const void* __restrict__ residual, int rdt,
+                               float* __restrict__ out_f32, void* __restrict__ out_act, int odt,
+                               uint8_t* smem, int bx, int t, Wait wait) {
     constexpr int RPS = 64 / LPR;                               // units per wave step
     constexpr int UPW = (KB * RR + 4 * RPS - 1) / (4 * RPS);  // steps per wave
     constexpr int NTB = 4;                                      // hidden quarter blocks per thread and round
     __shared__ float ys[KB][RR];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane / LPR, q = lane % LPR;
-    const int t = blockIdx.y, r0 = blockIdx.x * RR;
+    const int r0 = bx * RR;
     const int I = nb * 32;
     const int64_t row_bytes = (int64_t)nb * 18;
     uint32_t* dig = reinterpret_cast<uint32_t*>(smem);  // [K][16][nb] digit words
     float* dsc = reinterpret_cast<float*>(dig + K * 16 * nb);  // [K][nb] block scales
 
-    // a lane's slot k of the token (k clamped below K): its expert, each lane
-    // loading that of its own k (a few distinct addresses per wave); the hidden
-    // rows are stored by slot, t * K + k, so their loads need no routing
-    const int32_t* ids_t = ids + (int64_t)t * K;
     // hidden rows -> registers, one quarter block per task (unconditional,
-    // clamped loads so that their number is static)
+    // clamped loads so that their number is static); the hidden rows are
+    // stored by slot, t * K + k, so their loads need no routing
     const int ntask = K * nb * 4;
     float xv[NTB][8];
     auto load_h = [&](int round) {
@@ -714,7 +739,7 @@ __global__ __launch_bounds__(256) void decode_down_combine(
             const bool ok = task < ntask;
             const int m = task & 3, tb = task >> 2, k = tb / nb, b = tb % nb;
             const int64_t s = (int64_t)t * K + (ok ? k : 0);
-            load_quarter<ADT>(hbuf, s * I + b * 32, m, xv[i]);
+            load_quarter<ADT, COH>(hbuf, s * I + b * 32, m, xv[i]);
         }
     };
     auto digitize_h = [&](int round) {
@@ -727,9 +752,9 @@ __global__ __launch_bounds__(256) void decode_down_combine(
             }
         }
     };
-    load_h(0);
     // this lane's weight windows: unit u = (wave * UPW + s) * RPS + g is row
-    // u % RR of slot u / RR (units past the K slots load slot K-1's)
+    // u % RR of slot u / RR (units past the K slots load slot K-1's); each lane
+    // reads the expert of its own slot (a few distinct addresses per wave)
     const int qq = min(q, nb / 2 - 1);
     uint32_t wd[UPW][9];
 #pragma unroll
@@ -748,9 +773,11 @@ __global__ __launch_bounds__(256) void decode_down_combine(
     float ck[KB];
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
-        const int64_t s = (int64_t)t * K + min(k, K - 1);
-        ck[k] = tw[s] * (scale ? scale[ids[s]] : 1.f);
+        const int kk = min(k, K - 1);
+        ck[k] = w_t[kk] * (scale ? scale[ids_t[kk]] : 1.f);
     }
+    if (!wait()) return;
+    load_h(0);
     digitize_h(0);
     const int rounds = (ntask + 256 * NTB - 1) / (256 * NTB);
     for (int round = 1; round < rounds; ++round) {
@@ -790,6 +817,122 @@ __global__ __launch_bounds__(256) void decode_down_combine(
     }
 }
 
+template <int ADT, int LPR, int KB, int RR>
+__global__ __launch_bounds__(256) void decode_down_combine(
+    const uint8_t* __restrict__ Wd, int nb, int H, const void* __restrict__ hbuf,
+    const int32_t* __restrict__ ids, const float* __restrict__ tw,
+    const float* __restrict__ scale, int K,
+    const void* __restrict__ residual, int rdt, float* __restrict__ out_f32,
+    void* __restrict__ out_act, int odt) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int t = blockIdx.y;
+    down_combine_tile<ADT, LPR, KB, RR>(Wd, nb, H, hbuf, ids + (int64_t)t * K, tw + (int64_t)t * K, scale,
+                                        K, residual, rdt, out_f32, out_act, odt, smem, blockIdx.x, t,
+                                        [] { return true; });
+}
+
+// ---- one-token decode: gate/up and down in one launch ------------------------------
+// Workgroups 0 .. ng-1 are the gate/up tiles of decode_gate_up (bx = b % wgs,
+// by = b / wgs); workgroups ng .. ng+nd-1 the down + combine tiles of
+// decode_down_combine (output rows RR * (b - ng) ..).  A down workgroup routes
+// the token itself (the same selection as every gate/up workgroup), loads its
+// weight windows and combine factors, and only then waits until every gate/up
+// workgroup has stored its part of h.
+//
+// Hand-over without cache maintenance: h is stored with agent-scope relaxed
+// atomic stores and read with agent-scope relaxed atomic loads, both coherent
+// across the XCDs' L2 caches, so neither side needs an L2 write-back or
+// invalidate (each costs microseconds when hundreds of workgroups issue one).
+// A gate/up workgroup waits until its stores are acknowledged (vmcnt 0),
+// crosses a barrier and bumps counter b mod DECODE_CTR_LINES; the counters sit
+// on separate 256-byte lines, since hundreds of increments and polls on one
+// address serialise at its memory channel.  Wave 0 of a down workgroup polls
+// all counters (one per lane) until each has its share of ng.
+//
+// The down workgroups carry the highest block numbers and workgroups are
+// dispatched in order, so every gate/up workgroup is resident or finished
+// before any down workgroup waits; the wait is bounded all the same
+// (DECODE_WAIT_LIMIT polls, each a memory round trip and a short sleep: about
+// a second): on expiry the timeout flag (ctr[1]) is set and the workgroup
+// stores nothing.  The counters are zeroed by the router launch of the same
+// call.  Outputs equal the two-launch path's bit for bit.
+constexpr int DECODE_WAIT_LIMIT = 1 << 20;
+static_assert(DECODE_CTR_LINES <= 64, "one lane of wave 0 watches each counter");
+
+template <int ADT, int LPR, int UPW, int LPRD, int KB, int RR>
+__global__ __launch_bounds__(256) void decode_ffn_one(
+    const uint8_t* __restrict__ W, const uint8_t* __restrict__ Wd, int nb, int nbd, int I, int H,
+    const void* __restrict__ x, const float* __restrict__ logits, int E, int K,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, int32_t* __restrict__ off_out,
+    int32_t* __restrict__ ss_out, int32_t* __restrict__ sp_out, void* __restrict__ h,
+    int wave_lds_bytes, int wgs, int ng, int* __restrict__ ctr, const float* __restrict__ scale,
+    const void* __restrict__ residual, int rdt, float* __restrict__ out_f32,
+    void* __restrict__ out_act, int odt) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ DecodeRouting R;
+    __shared__ int s_ok;
+    const int b = blockIdx.x;
+    if (b < ng) {
+        const int bx = b % wgs, by = b / wgs;
+        auto route = [&](int, int& e, int& p0, int& n) {
+            decode_route(logits, 1, E, K, R);
+            if (b == 0) {
+                const int tid = threadIdx.x;
+                if (tid < K) {
+                    ids_out[tid] = R.ids[tid];
+                    w_out[tid] = R.w[tid];
+                    ss_out[tid] = R.ss[tid];
+                    sp_out[tid] = R.sp[tid];
+                }
+                for (int xx = tid; xx <= E; xx += 256) off_out[xx] = R.off[xx];
+            }
+            // K distinct experts, one slot each, the by-th in sorted order
+            p0 = by;
+            n = 1;
+            e = R.ids[R.ss[by]];
+            return true;
+        };
+        gemv_tile<0, ADT, LPR, 1, UPW, true, false, true, true, true>(
+            W, nb, I, H, x, R.off, R.ss, K, E, h, wave_lds_bytes, smem, bx, by, route);
+        // the agent-scope stores of h are complete (acknowledged) before the
+        // barrier, so the increment after it publishes them without an L2
+        // write-back
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_add(ctr + DECODE_CTR_STRIDE * (b % DECODE_CTR_LINES), 1,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    decode_route(logits, 1, E, K, R);
+    auto wait = [&]() {
+        if (threadIdx.x < 64) {
+            // lane j < DECODE_CTR_LINES watches counter j, which gate/up
+            // workgroups b = j mod DECODE_CTR_LINES bump
+            const int j = threadIdx.x;
+            const int need = j < DECODE_CTR_LINES
+                                 ? ng / DECODE_CTR_LINES + (j < ng % DECODE_CTR_LINES ? 1 : 0)
+                                 : 0;
+            int* cj = ctr + DECODE_CTR_STRIDE * min(j, DECODE_CTR_LINES - 1);
+            int it = 0;
+            while (__ballot(j < DECODE_CTR_LINES &&
+                            __hip_atomic_load(cj, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) &&
+                   it < DECODE_WAIT_LIMIT) {
+                __builtin_amdgcn_s_sleep(1);
+                ++it;
+            }
+            if (j == 0) {
+                s_ok = it < DECODE_WAIT_LIMIT;
+                if (!s_ok) __hip_atomic_store(ctr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        __syncthreads();
+        return s_ok != 0;
+    };
+    down_combine_tile<ADT, LPRD, KB, RR, true>(Wd, nbd, H, h, R.ids, R.w, scale, K, residual, rdt, out_f32,
+                                         out_act, odt, smem, b - ng, 0, wait);
+}
+
 // output rows per workgroup of the fused down + combine (a divisor of 64)
 constexpr int DECODE_DOWN_ROWS = 16;
 
@@ -820,9 +963,33 @@ hipError_t launch_decode_layer(const void* x, int x_dt, int T, int H, const floa
                                int K, const uint8_t* w_gate_up, const uint8_t* w_down, int I,
                                const float* scale, int32_t* ids, float* w, int32_t* off,
                                int32_t* ss, int32_t* sp, const void* residual, int rdt,
-                               float* out_f32, void* out_act, int odt, void* h_ws,
+                               float* out_f32, void* out_act, int odt, void* h_ws, int* ctr,
                                hipStream_t st) {
     const int N = T * K, n_active = min(E, N);
+    // one token, gate/up rows of 33..64 block pairs (LPR 64), down rows of 9..16
+    // (LPR 16), at most 8 experts: gate/up and down in one launch
+    if (T == 1 && K <= 8 && ctr && H / 64 > 32 && H / 64 <= 64 && I / 64 > 8 && I / 64 <= 16) {
+        constexpr int LPR = 64, LPRD = 16, KB = 8, RR = DECODE_DOWN_ROWS;
+        constexpr int UPW = steps_per_wave<0, LPR, false>();
+        constexpr int RPW = (64 / LPR) * UPW;
+        constexpr int NCH = (RPW * 36 * LPR + 15 + 1023) / 1024;
+        const int nb = H / 32, nbd = I / 32;
+        const int wgs = (I + 4 * RPW - 1) / (4 * RPW), ng = wgs * n_active, nd = H / RR;
+        const int wave_lds = 2 * NCH * 1024;
+        const size_t lds = std::max((size_t)4 * wave_lds + (size_t)nb * 17 * sizeof(uint32_t),
+                                    decode_down_lds_bytes(K, I));
+        auto go = [&](auto adt) {
+            constexpr int A = decltype(adt)::value;
+            decode_ffn_one<A, LPR, UPW, LPRD, KB, RR><<<ng + nd, 256, lds, st>>>(
+                w_gate_up, w_down, nb, nbd, I, H, x, logits, E, K, ids, w, off, ss, sp, h_ws, wave_lds,
+                wgs, ng, ctr, scale, residual, rdt, out_f32, out_act, odt);
+        };
+        if (x_dt == MOE_F32)
+            go(std::integral_constant<int, MOE_F32>{});
+        else
+            go(std::integral_constant<int, MOE_BF16>{});
+        return hipGetLastError();
+    }
     // gate/up: the expert FFN's choice of chunk size and load path
     auto gu = [&](auto adt, auto tc, auto direct, auto one) {
         constexpr int A = decltype(adt)::value, TC = decltype(tc)::value;

@@ -11,9 +11,22 @@ constexpr int PERM_TILE = 1024;        // permutation: slots per tile (256 threa
 constexpr int DIGIT_NMAX = 30583;       // largest |n| with 4 balanced base-16 digits: 7*(1+16+256+4096)
 constexpr int FFN_MFMA_MIN_T = 64;     // expert FFN: bf16 MFMA grouped GEMM from this many tokens
 
+// The one-token decode's completion counters: DECODE_CTR_LINES ints, one per
+// 256-byte line (int index DECODE_CTR_STRIDE * j), so that the increments of
+// many workgroups and the polls spread over several memory channels; int 1 is
+// the timeout flag.  The header takes DECODE_CTR_BYTES of the workspace.
+constexpr int DECODE_CTR_LINES = 64;
+constexpr int DECODE_CTR_STRIDE = 64;
+constexpr size_t DECODE_CTR_BYTES = DECODE_CTR_LINES * DECODE_CTR_STRIDE * sizeof(int);
+// int index of the i-th word to clear, i < DECODE_CTR_LINES + 1
+__host__ __device__ inline int decode_ctr_word(int i) { return i < DECODE_CTR_LINES ? DECODE_CTR_STRIDE * i : 1; }
+
+// zero_ctr (optional): a decode counter header that the launch clears (zeroed
+// by the router launch of the same call)
 hipError_t launch_router_logits(const void* x, int x_dt, int64_t T, int H, const float* W,
                                 const float* rsc, const float* bias, int E, float* logits,
-                                hipStream_t st);
+                                hipStream_t st, int* zero_ctr = nullptr);
+hipError_t launch_zero_decode_ctr(int* p, hipStream_t st);
 hipError_t launch_route_small(const void* x, int x_dt, int T, int H, const float* W,
                               const float* rsc, const float* bias, int E, int K, float* logits,
                               int32_t* ids, float* w, int32_t* offsets, int32_t* sorted_slots,
@@ -32,13 +45,14 @@ hipError_t launch_ffn_gemv(const void* x, int x_dt, int64_t T, int H, const uint
 
 // one decode layer (router logits, gate/up with the routing inside, down with
 // the combine inside): up to ROUTER_GEMV_MAX_T tokens and 64 slots, rows of an
-// even number of Q4_0 blocks
+// even number of Q4_0 blocks.  ctr: two ints, zero on entry (the one-token
+// one-launch path's completion counter and timeout flag)
 bool decode_layer_supported(int64_t T, int H, int I, int K);
 hipError_t launch_decode_layer(const void* x, int x_dt, int T, int H, const float* logits, int E,
                                int K, const uint8_t* w_gate_up, const uint8_t* w_down, int I,
                                const float* scale, int32_t* ids, float* w, int32_t* off,
                                int32_t* ss, int32_t* sp, const void* residual, int rdt,
-                               float* out_f32, void* out_act, int odt, void* h_ws,
+                               float* out_f32, void* out_act, int odt, void* h_ws, int* ctr,
                                hipStream_t st);
 
 // bf16 activations, enough tokens, and rows of an even number of Q4_0 blocks

@@ -102,9 +102,12 @@ __global__ __launch_bounds__(256) void router_logits_gemv(const void* __restrict
                                                           const float* __restrict__ W,
                                                           const float* __restrict__ rsc,
                                                           const float* __restrict__ bias, int E,
-                                                          float* __restrict__ logits) {
+                                                          float* __restrict__ logits,
+                                                          int* __restrict__ zero_ctr) {
     __shared__ float part[4][ROUTER_GEMV_MAX_T];
     const int e = blockIdx.x;
+    if (zero_ctr && e == 0 && blockIdx.y == 0 && threadIdx.x <= DECODE_CTR_LINES)
+        zero_ctr[decode_ctr_word(threadIdx.x)] = 0;
     const int t0 = blockIdx.y * ROUTER_GEMV_MAX_T, tg = min(ROUTER_GEMV_MAX_T, T - t0);
     const void* xg = XDT == MOE_F32 ? (const void*)((const float*)x + (int64_t)t0 * H)
                                     : (const void*)((const uint16_t*)x + (int64_t)t0 * H);
@@ -549,9 +552,23 @@ __global__ __launch_bounds__(NW * 64) void router_logits_mfma_batch(
     }
 }
 
+__global__ void zero_decode_ctr(int* __restrict__ p) {
+    if ((int)threadIdx.x <= DECODE_CTR_LINES) p[decode_ctr_word(threadIdx.x)] = 0;
+}
+
+hipError_t launch_zero_decode_ctr(int* p, hipStream_t st) {
+    zero_decode_ctr<<<1, 128, 0, st>>>(p);
+    return hipGetLastError();
+}
+
 hipError_t launch_router_logits(const void* x, int x_dt, int64_t T, int H, const float* W,
                                 const float* rsc, const float* bias, int E, float* logits,
-                                hipStream_t st) {
+                                hipStream_t st, int* zero_ctr) {
+    // only the few-token kernel below zeroes the counter itself
+    if (zero_ctr && T >= ROUTER_MFMA_MIN_T) {
+        const hipError_t e = launch_zero_decode_ctr(zero_ctr, st);
+        if (e != hipSuccess) return e;
+    }
     if (x_dt == MOE_BF16 && T >= ROUTER_MFMA_MIN_T && E % 32 == 0) {
         // 32 tokens x 32 experts per workgroup, K split over 4 waves (over 8 when
         // the tiles are too few to fill the chip); many tokens: ROUTER_WIDE_TF
@@ -584,7 +601,7 @@ hipError_t launch_router_logits(const void* x, int x_dt, int64_t T, int H, const
         dim3 grid(E, (unsigned)((T + ROUTER_GEMV_MAX_T - 1) / ROUTER_GEMV_MAX_T));
         router_variant(x_dt, (int)T, rsc != nullptr, [&](auto xdt, auto tt, auto r) {
             router_logits_gemv<decltype(xdt)::value, decltype(tt)::value, decltype(r)::value>
-                <<<grid, 256, 0, st>>>(x, (int)T, H, W, rsc, bias, E, logits);
+                <<<grid, 256, 0, st>>>(x, (int)T, H, W, rsc, bias, E, logits, zero_ctr);
         });
     } else {
         dim3 grid((unsigned)((T + RT_BM - 1) / RT_BM), (E + RT_BN - 1) / RT_BN);

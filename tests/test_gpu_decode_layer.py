@@ -10,6 +10,10 @@
   * a 30-layer decode stack (RMSNorm, layer, residual) captured in one HIP
     graph and replayed several times, with eager work between the replays,
     each replay equal to the eager stack bit for bit.
+
+One token at the Gemma shape runs gate/up and down in one launch (down
+workgroups wait on a completion counter); every call here also checks that
+its timeout flag stayed clear.  Other shapes take two launches.
 """
 import numpy as np
 import pytest
@@ -59,6 +63,10 @@ def _run_both(L, logits_in=None, residual=False):
             binding.moe_layer_decode(d["x"], d["wr"], d["gu"], d["dn"], spec.K, expert_scale=d["sc"],
                                      logit_bias=d["bias"], bufs=bufs, logits_in=li,
                                      out_act=out_act, residual=res)
+            torch.cuda.synchronize()
+            # the one-token one-launch path's completion counter and timeout flag
+            ctr = bufs.ws_decode[:8].view(torch.int32).cpu().numpy()
+            assert ctr[1] == 0, "the down workgroups timed out waiting for gate/up"
         else:
             binding.moe_layer(d["x"], d["wr"], d["gu"], d["dn"], spec.K, expert_scale=d["sc"],
                               logit_bias=d["bias"], bufs=bufs, logits_in=li, out_act=out_act,
@@ -102,6 +110,7 @@ def test_decode_layer_injected_logits_bitwise():
 
 
 @pytest.mark.parametrize("H,I,E,K,T,act", [
+    (256, 64, 8, 2, 1, "f32"),       # one token, a shape outside the one-launch path
     (256, 64, 8, 2, 4, "f32"),       # one block pair per down row
     (384, 192, 16, 16, 4, "bf16"),   # K = 16 (64 slots), odd pair counts
     (512, 128, 32, 4, 7, "bf16"),
