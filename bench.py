@@ -482,7 +482,7 @@ def bench_layer(spec, steps: int, warmup: int, nsets: int, cpu_seconds: float = 
     # S consecutive steps per HIP graph (like consecutive layers of a model in
     # one graph), so that the timed loop does not measure the host's per-replay
     # launch cost; graph j holds steps S j .. S j + S - 1
-    S = 8 if T <= 64 and steps % 8 == 0 and G % 8 == 0 else 1
+    S = next(s for s in (8, 4, 2, 1) if T <= 64 and steps % s == 0 and G % s == 0 or s == 1)
     NG = G // S
     graphs = []
     for j in range(NG):

@@ -40,10 +40,13 @@ MOE_DEV float f16_bits_to_f32(uint32_t h) {
 
 // ---- device-coherent accesses ------------------------------------------------------
 // Data passed between workgroups of one launch goes through agent-scope relaxed
-// atomic stores and loads (coherent across the chip's L2 slices); the counter
-// that publishes it is an agent-scope release increment, which orders the
-// producer's stores before it, and the consumer that sees the final count
-// issues an agent-scope acquire fence before its loads.
+// atomic stores and loads, whose scope bits make the hardware keep them
+// coherent across the vector L1 and the XCDs' separate L2s.  The producer waits until its stores are
+// acknowledged (s_waitcnt vmcnt(0)) and then bumps a counter with a relaxed
+// atomic; the consumer issues its coherent loads only after it has seen the
+// final count.  Neither side needs an L2 write-back or invalidate, which an
+// agent-scope release or acquire would issue (microseconds each when many
+// workgroups issue one).
 MOE_DEV void coherent_store(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

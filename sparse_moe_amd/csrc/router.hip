@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void router_logits_tiled(const void* __restric
     }
 }
 
-// --------------------------------------------------------------------------// Top-K: one wave per token.
+// ---- top-K: one wave per token ---------------------------------------------
 __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ logits, int64_t T,
                                                     int E, int K, int32_t* __restrict__ ids,
                                                     float* __restrict__ w) {
@@ -229,13 +229,14 @@ __global__ __launch_bounds__(256) void route_small(const void* __restrict__ x, i
     }
     __shared__ int s_last;
     // The logits are stored by threads t < T <= 8, all in wave 0, which also
-    // makes the count: its release (agent scope) orders them before the
-    // increment, and the last workgroup's acquire fence (after it has seen
-    // every other increment) orders its reads after them.
+    // makes the count: the wave waits until its coherent stores are
+    // acknowledged, then increments; the last workgroup reads them with
+    // coherent loads issued after its increment has returned.  No L2
+    // write-back or invalidate is needed on either side.
+    if (threadIdx.x < 64) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (threadIdx.x == 0) {
-        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old == (int)gridDim.x - 1);
-        if (s_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
     if (!s_last) return;
