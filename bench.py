@@ -31,7 +31,7 @@ Q4_0_EXPERT_BYTES = lambda H, I: 3 * H * I // 32 * 18   # [gate; up] + down
 # stored PMC traffic is reported only while the kernel sources are unchanged
 KERNEL_SOURCE_DIR = "sparse_moe_amd/csrc"
 # kernels of the call the roofline times: the decode layer call, or the expert FFN
-DECODE_KERNELS = ("router_logits_gemv", "decode_gate_up", "decode_down_combine")
+DECODE_KERNELS = ("router_logits_gemv", "decode_ffn_one", "decode_gate_up", "decode_down_combine")
 FFN_KERNELS = ("ffn_gemv_q4_0", "ffn_mfma")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_traffic.json")
 
@@ -557,8 +557,12 @@ def bench_layer(spec, steps: int, warmup: int, nsets: int, cpu_seconds: float = 
         call_bytes = sum(d * expert_bytes + E * H * 4 + T * H * asz + E * 4 + T * H * 4
                          for d in distinct[:F]) / F
         achieved = call_bytes / (ffn_ms * 1e-3) / 1e9
-        roofline = {"kernel": "moe_layer_decode (router logits, gate/up GEMV with top-K and "
-                              "permutation inside, down GEMV with the combine inside: 3 launches)",
+        launches = ("router logits, then gate/up and down in one launch (top-K inside every "
+                    "workgroup, h handed over through completion counters): 2 launches"
+                    if T == 1 else
+                    "router logits, gate/up GEMV with top-K and permutation inside, down GEMV "
+                    "with the combine inside: 3 launches")
+        roofline = {"kernel": "moe_layer_decode (%s)" % launches,
                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                     "bytes_per_launch": call_bytes, "avg_launch_us": ffn_ms * 1e3}
