@@ -116,6 +116,69 @@ MOE_DEV f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// One stage (a pair of Q4_0 blocks) of a wave's products: NF 16-row weight
+// fragments (48-byte rows from WL) against MF 16-slot fragments of the staged
+// activations Sa [2][AROWS][64 B] with their sums Sc [2][AROWS], added into acc.
+template <int MF, int NF, int AROWS>
+MOE_DEV void stage_products(const uint8_t* __restrict__ Sa, const float* __restrict__ Sc,
+                            const uint8_t* __restrict__ WL, int g, int l16, int swz, int q1off,
+                            uint32_t nib_mask, f32x4 (&acc)[MF][NF]) {
+    // The weight words of both blocks are read first, so the LDS round
+    // trips of block 1 pass under block 0's MFMAs (read per block, each
+    // block began with four dependent reads in turn).  Block 0: the scale
+    // and bytes 2 + 4g .. 5 + 4g of the pair (two dwords and an
+    // alignbyte); block 1: the scale and bytes 20 + 4g .. 23 + 4g.
+    uint32_t w0lo[NF], w0hi[NF], w1q[NF], d0b[NF], d1b[NF];
+#pragma unroll
+    for (int nf = 0; nf < NF; ++nf) {
+        const uint8_t* rp = WL + nf * 16 * 48;
+        w0lo[nf] = *(const uint32_t*)(rp + 4 * g);
+        w0hi[nf] = *(const uint32_t*)(rp + 4 * g + 4);
+        d0b[nf] = *(const uint16_t*)rp;
+    }
+#pragma unroll
+    for (int nf = 0; nf < NF; ++nf) {
+        const uint8_t* rp = WL + nf * 16 * 48;
+        w1q[nf] = *(const uint32_t*)(rp + q1off);
+        d1b[nf] = *(const uint16_t*)(rp + 18);
+    }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        float dv[NF];
+        u32x4 bq[NF];
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) {
+            if (blk == 0) {
+                dv[nf] = f16_bits_to_f32((uint16_t)d0b[nf]);
+                bq[nf] = dq_group(__builtin_amdgcn_alignbyte(w0hi[nf], w0lo[nf], 2), nib_mask);
+            } else {
+                dv[nf] = f16_bits_to_f32((uint16_t)d1b[nf]);
+                bq[nf] = dq_group(w1q[nf], nib_mask);
+            }
+            // keep the scale a plain fp32 register: otherwise the compiler folds
+            // the fp16 conversion into v_fma_mix_f32 for every scale FMA, which
+            // issues slower and raises register pressure into spills
+            asm volatile("" : "+v"(dv[nf]));
+        }
+        // every slot fragment, unconditionally (rows past the count are computed
+        // and dropped at the store): per-fragment branches cost registers and
+        // serialise the schedule
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf) {
+            const u32x4 a =
+                *(const u32x4*)(Sa + blk * AROWS * 64 + (mf * 16 + l16) * 64 + swz);
+            const f32x4 c = *(const f32x4*)&Sc[blk * AROWS + mf * 16 + 4 * g];
+            f32x4 t[NF];
+#pragma unroll
+            for (int nf = 0; nf < NF; ++nf) t[nf] = mfma_bf16(a, bq[nf], c);
+#pragma unroll
+            for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mf][nf][i] = fmaf(dv[nf], t[nf][i], acc[mf][nf][i]);
+        }
+    }
+}
+
 // Tile lookup.  Slot tiles cover an expert's slots MT at a time (the last one
 // partial); each has n_tiles column tiles.
 // The grid is an upper bound, so the numbering is made once the real counts
@@ -473,48 +536,8 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         uint32_t nib_mask;
         asm volatile("v_mov_b32 %0, 0x00780078" : "=v"(nib_mask));
         auto compute = [&](const StageRef& S) {
-            const uint8_t* WL = S.w + (wave * 64 + l16) * 48;
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                // this block's weights: the scale and the lane's qs dword (block 0:
-                // bytes 2 + 4g .. 5 + 4g of the pair, two dwords and an alignbyte;
-                // block 1: bytes 20 + 4g .. 23 + 4g)
-                float dv[NF];
-                u32x4 bq[NF];
-#pragma unroll
-                for (int nf = 0; nf < NF; ++nf) {
-                    const uint8_t* rp = WL + nf * 16 * 48;
-                    if (blk == 0) {
-                        const uint32_t lo = *(const uint32_t*)(rp + 4 * g);
-                        const uint32_t hi = *(const uint32_t*)(rp + 4 * g + 4);
-                        dv[nf] = f16_bits_to_f32(*(const uint16_t*)rp);
-                        bq[nf] = dq_group(__builtin_amdgcn_alignbyte(hi, lo, 2), nib_mask);
-                    } else {
-                        dv[nf] = f16_bits_to_f32(*(const uint16_t*)(rp + 18));
-                        bq[nf] = dq_group(*(const uint32_t*)(rp + q1off), nib_mask);
-                    }
-                    // keep the scale a plain fp32 register: otherwise the compiler folds
-                    // the fp16 conversion into v_fma_mix_f32 for every scale FMA, which
-                    // issues slower and raises register pressure into spills
-                    asm volatile("" : "+v"(dv[nf]));
-                }
-                // every slot fragment, unconditionally (rows past the count are computed
-                // and dropped at the store): per-fragment branches cost registers and
-                // serialise the schedule
-#pragma unroll
-                for (int mf = 0; mf < MF; ++mf) {
-                    const u32x4 a =
-                        *(const u32x4*)(S.a + blk * AROWS * 64 + (mf * 16 + l16) * 64 + swz);
-                    const f32x4 c = *(const f32x4*)&S.c[blk * AROWS + mf * 16 + 4 * g];
-                    f32x4 t[NF];
-#pragma unroll
-                    for (int nf = 0; nf < NF; ++nf) t[nf] = mfma_bf16(a, bq[nf], c);
-#pragma unroll
-                    for (int nf = 0; nf < NF; ++nf)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[mf][nf][i] = fmaf(dv[nf], t[nf][i], acc[mf][nf][i]);
-                }
-            }
+            stage_products<MF, NF, AROWS>(S.a, S.c, S.w + (wave * 64 + l16) * 48, g, l16, swz, q1off, nib_mask,
+                                          acc);
         };
         // One step per pair: issue the loads of a later pair (none past the
         // last), compute this pair, wait for this wave's loads of the next pair,

@@ -243,15 +243,18 @@ def test_mfma_tile_size_boundaries(I):
     assert np.array_equal(np.diff(g["offsets"]), np.array(counts)), np.diff(g["offsets"])
 
 
-def test_mfma_tile_boundaries_among_many_experts():
+@pytest.mark.parametrize("H,I", [(256, 512), (64, 64), (128, 192)])
+def test_mfma_tile_boundaries_among_many_experts(H, I):
     # The slot counts above (1, 32, 33, 64, 65, 96, 97, 129) among 128 more
     # experts of 384 slots each (three full tiles): the tile numbering and the
-    # XCD runs over a few hundred tiles, with every tile variant present.
+    # XCD runs over a few hundred tiles, with every tile variant present.  The
+    # shapes give the two-stage ring 4, 1 and 2 block pairs (gate/up) and 8, 1
+    # and 3 (down), and leave waves without rows in the last column tile.
     # Injected logits fix every token's expert; outputs are checked on the first
     # and last token of the eight boundary experts and of a few others.
     counts = [1, 32, 33, 64, 65, 96, 97, 129] + [384] * 128
     T, E = sum(counts), len(counts)
-    spec = synth.LayerSpec("tile-bounds-many", H=256, E=E, K=1, I=512, T=T, act="bf16",
+    spec = synth.LayerSpec("tile-bounds-many-H%d-I%d" % (H, I), H=H, E=E, K=1, I=I, T=T, act="bf16",
                            router_std=1 / 16, seed=37)
     L = synth.make_layer(spec)
     rng = np.random.default_rng(41)
