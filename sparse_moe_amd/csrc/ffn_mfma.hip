@@ -38,6 +38,9 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int MT = 128;        // slots per tile
+// In the XCD-run numbering an expert's last tile takes up to MTX slots (10
+// fragments of 16) instead of leaving a tile of at most 32 slots behind.
+constexpr int MTX = 160;
 constexpr int NT = 256;        // weight rows per tile (64 per wave)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -217,11 +220,12 @@ MOE_DEV int scan_incl(int v, int lane) {
     return v;
 }
 
-__device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid, int n_tiles, int* s_res,
-                          int& e_out, int& base, int& cnt, int& ntile, bool& half) {
+__device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid, int n_tiles, int mtx,
+                          int* s_res, int& e_out, int& base, int& cnt, int& ntile, bool& half) {
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
         int c[4], full[4], rem[4], u[4], tot = 0;
+        int nm[4], um[4], totm = 0;  // slot tiles with a merged last tile, their units
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int e = lane * 4 + q;
@@ -230,27 +234,34 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid, i
             rem[q] = c[q] - full[q] * MT;
             u[q] = (full[q] + (rem[q] ? 1 : 0)) * n_tiles;  // column tiles
             tot += u[q];
+            nm[q] = c[q] <= mtx ? (c[q] > 0 ? 1 : 0) : 1 + (c[q] - mtx + MT - 1) / MT;
+            um[q] = nm[q] * n_tiles;
+            totm += um[q];
         }
         const int incl = scan_incl(tot, lane);
         const int total = __shfl(incl, 63);  // workgroups with a tile
         // this lane's find: expert, its slot tile, column tile
-        int e_sel = -1, k_sel = 0, c_sel = 0, nt_sel = 0;
+        int e_sel = -1, k_sel = 0, c_sel = 0, nt_sel = 0, n_sel = 0;
         const bool many = total > FFN_MFMA_LPT_UNITS;
         if (many) {
-            const int per_xcd = (total + 7) >> 3;
+            // tiles of MT slots, the last of up to mtx
+            const int inclm = scan_incl(totm, lane);
+            const int totalm = __shfl(inclm, 63);
+            const int per_xcd = (totalm + 7) >> 3;
             const int lin = (bid & 7) * per_xcd + (bid >> 3);
-            const bool have = (bid >> 3) < per_xcd && lin < total;
-            int run = incl - tot;
+            const bool have = (bid >> 3) < per_xcd && lin < totalm;
+            int run = inclm - totm;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                if (have && lin >= run && lin < run + u[q]) {
+                if (have && lin >= run && lin < run + um[q]) {
                     const int ue = lin - run;
                     e_sel = lane * 4 + q;
                     c_sel = c[q];
+                    n_sel = nm[q];
                     k_sel = ue / n_tiles;
                     nt_sel = ue - k_sel * n_tiles;
                 }
-                run += u[q];
+                run += um[q];
             }
         } else {
             // tiles per class: class 0 holds an expert's full tiles and a
@@ -313,7 +324,7 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bid, i
         if (e_sel >= 0) {
             s_res[0] = e_sel;
             s_res[1] = offsets[e_sel] + k_sel * MT;
-            s_res[2] = min(MT, c_sel - k_sel * MT);
+            s_res[2] = many ? (k_sel == n_sel - 1 ? c_sel - k_sel * MT : MT) : min(MT, c_sel - k_sel * MT);
             s_res[3] = nt_sel;
             s_res[4] = !many && c_sel - k_sel * MT <= FFN_MFMA_LIGHT;
         }
@@ -382,13 +393,13 @@ __global__ __launch_bounds__(256) void ffn_mfma(
     const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_slots, int K, int E, uint16_t* __restrict__ h_out,
     float* __restrict__ hsum_out, float* __restrict__ y_out) {
-    __shared__ __attribute__((aligned(16))) uint8_t a0[2 * MT * 64], a1[2 * MT * 64];
-    __shared__ __attribute__((aligned(16))) float cc0[2 * MT], cc1[2 * MT];
+    __shared__ __attribute__((aligned(16))) uint8_t a0[2 * MTX * 64], a1[2 * MTX * 64];
+    __shared__ __attribute__((aligned(16))) float cc0[2 * MTX], cc1[2 * MTX];
     __shared__ __attribute__((aligned(16))) uint8_t w0[NT * 48], w1[NT * 48];
-    // third stage of the light ring (tiles of at most 32 slots)
-    __shared__ __attribute__((aligned(16))) uint8_t la2[2 * 32 * 64];
-    __shared__ __attribute__((aligned(16))) float lc2[2 * 32];
-    __shared__ __attribute__((aligned(16))) uint8_t w2[NT * 48];
+    // the third stage of the light ring (tiles of at most 32 slots) lives in the
+    // parts of stage 0's activation and sum arrays that a light tile leaves free
+    static_assert(2 * 32 * 64 + 2 * 32 * 64 + NT * 48 <= 2 * MTX * 64 && 2 * 32 + 2 * 32 <= 2 * MTX,
+                  "light third stage fits");
     struct StageRef {
         uint8_t* a;
         float* c;
@@ -399,7 +410,11 @@ __global__ __launch_bounds__(256) void ffn_mfma(
 
     int e, base, cnt, ntile;
     bool half;
-    if (!find_tile(offsets, E, blockIdx.x, n_tiles, s_res, e, base, cnt, ntile, half)) return;
+    // the merged last tile (up to MTX slots) only where the loads are buffer
+    // loads: the 64-bit-address variant would exceed 256 VGPRs with its 10
+    // fragments (and run one wave per SIMD)
+    constexpr int MX = BUF ? MTX : MT;
+    if (!find_tile(offsets, E, blockIdx.x, n_tiles, MX, s_res, e, base, cnt, ntile, half)) return;
     e = __builtin_amdgcn_readfirstlane(e);
     base = __builtin_amdgcn_readfirstlane(base);
     cnt = __builtin_amdgcn_readfirstlane(cnt);
@@ -412,18 +427,17 @@ __global__ __launch_bounds__(256) void ffn_mfma(
     const uint8_t* We = W + (size_t)e * rows_e * rowbytes;
     const int npairs = nb >> 1;
 
-    // block sums: wave w loads block w >> 1 of tile rows 64 (w & 1) + lane
-    int64_t cbyte0;  // byte offset in csum
-    {
-        const int r = 64 * (wave & 1) + lane;
+    // byte offset in csum of entry P of a stage's block sums [2 blocks][rows]
+    auto sum_byte = [&](int P, int rows) -> int64_t {
+        const int blk = P / rows, r = P - blk * rows;
         const int p = base + min(r, cnt - 1);
         const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
-        cbyte0 = (arow * cs_row + (int64_t)(wave >> 1) * cs_blk) * 4;
-    }
+        return (arow * cs_row + (int64_t)blk * cs_blk) * 4;
+    };
     // buffer resources (unbounded: every offset stays inside its buffer)
     const i32x4 r_act = buffer_rsrc(act), r_cs = buffer_rsrc(csum), r_w = buffer_rsrc(We);
 
-    const int mfa = min(8, (cnt + 15) >> 4);  // valid slot fragments
+    const int mfa = min(MX / 16, (cnt + 15) >> 4);  // valid slot fragments
 
     // The main loop and epilogue for MF slot fragments (16 slots each).  A tile
     // of at most 32, 64 or 96 slots (an expert's last, partial tile, or a small
@@ -431,9 +445,12 @@ __global__ __launch_bounds__(256) void ffn_mfma(
     // the activation loads, MFMAs and scale FMAs of a full tile.
     auto run = [&](auto mf_const, auto nf_const) {
         constexpr int MF = decltype(mf_const)::value;
-        constexpr int NA = MF / 2;  // activation loads per wave per pair
+        // activation loads per wave per pair: the workgroup's 2 MF, the last one
+        // repeated by a wave past them (MF = 9)
+        constexpr int NA = (2 * MF + 3) / 4;
         constexpr bool LIGHT = MF == 2;
-        constexpr int AROWS = LIGHT ? 32 : MT;  // rows per block in a stage
+        constexpr bool WIDE = MF > MT / 16;  // a merged last tile of more than MT slots
+        constexpr int AROWS = LIGHT ? 32 : WIDE ? MTX : MT;  // rows per block in a stage
         // 16-row weight fragments per wave: 4, or 2 in a light tile's
         // half-width column tiles
         constexpr int NF = decltype(nf_const)::value;
@@ -482,7 +499,7 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         int adst[NA];
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
-            const int t = NA * wave + i, blk = t / MF, rg = t % MF;
+            const int t = min(NA * wave + i, 2 * MF - 1), blk = t / MF, rg = t % MF;
             const int r = 16 * rg + (lane >> 2);
             const int p = base + min(r, cnt - 1);
             const int64_t arow = MODE == 0 ? (int64_t)(sorted_slots[p] / K) : (int64_t)p;
@@ -490,11 +507,14 @@ __global__ __launch_bounds__(256) void ffn_mfma(
             abyte[i] = (arow * apitch + blk * 32 + 8 * chunk) * 2;
             adst[i] = blk * AROWS * 64 + rg * 1024;
         }
-        // block sums: a heavy stage takes block w >> 1 of rows 64 (w & 1) + lane
-        // from wave w; a light stage its 2 x 32 sums (block lane >> 5, row
-        // lane & 31) from every wave alike (the same bytes, so the four copies
-        // agree)
-        int64_t cbyte = cbyte0;
+        // block sums: a heavy stage takes entries 64 w + lane from wave w (block
+        // w >> 1 of rows 64 (w & 1) + lane when AROWS = MT), and in a wide one
+        // wave 0 also entries 2 AROWS - 64 + lane (the last rows of block 1,
+        // where the two overlap the same sums); a light stage its 2 x 32 sums
+        // (block lane >> 5, row lane & 31) from every wave alike (the same
+        // bytes, so the four copies agree)
+        int64_t cbyte = sum_byte(64 * wave + lane, AROWS);
+        const int64_t cbyte_x = WIDE ? sum_byte(2 * AROWS - 64 + lane, AROWS) : 0;
         int cdst = 64 * wave;
         if constexpr (LIGHT) {
             const int r = lane & 31;
@@ -511,6 +531,8 @@ __global__ __launch_bounds__(256) void ffn_mfma(
 #pragma unroll
                 for (int i = 0; i < NA; ++i) dma16(S.a + adst[i], (uint32_t)abyte[i], r_act, 128u * j);
                 dma4(S.c + cdst, (uint32_t)cbyte, r_cs, (uint32_t)(cpair * j));
+                if (WIDE && wave == 0)
+                    dma4(S.c + 2 * AROWS - 64, (uint32_t)cbyte_x, r_cs, (uint32_t)(cpair * j));
 #pragma unroll
                 for (int i = 0; i < NWL; ++i) dma16(S.w + 64 * 48 * wave + 1024 * i, woff[i], r_w, 36u * j);
             } else {
@@ -522,6 +544,9 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                                                      (lds_void_t*)(S.a + adst[i]), 16, 0, 0);
                 __builtin_amdgcn_global_load_lds((glb_void_t*)(cs_b + cbyte + (int64_t)cpair * j),
                                                  (lds_void_t*)(S.c + cdst), 4, 0, 0);
+                if (WIDE && wave == 0)
+                    __builtin_amdgcn_global_load_lds((glb_void_t*)(cs_b + cbyte_x + (int64_t)cpair * j),
+                                                     (lds_void_t*)(S.c + 2 * AROWS - 64), 4, 0, 0);
 #pragma unroll
                 for (int i = 0; i < NWL; ++i)
                     __builtin_amdgcn_global_load_lds(
@@ -546,7 +571,7 @@ __global__ __launch_bounds__(256) void ffn_mfma(
             // three stages (the third in arrays of its own): step j issues pair
             // j+2 into the stage pair j-1 used and waits for pair j+1 (issued a
             // step earlier)
-            const StageRef st2{la2, lc2, w2};
+            const StageRef st2{a0 + 2 * 32 * 64, cc0 + 2 * 32, a0 + 2 * 2 * 32 * 64};
             constexpr int OPS = NA + 1 + NWL;  // direct loads per wave per pair
             auto step = [&](const StageRef& cur, const StageRef& nxt, int j) {
                 const bool more = j + 2 < npairs;
@@ -645,10 +670,11 @@ __global__ __launch_bounds__(256) void ffn_mfma(
             // down product's K, written in the MFMA order with its sum.  Each slot
             // fragment's 16 rows of 64 bytes go through a stage array of the wave's
             // own (rows 80 bytes apart, so the 4 lane groups' writes fall in
-            // different banks) and leave as one 16-byte store per lane.
+            // different banks; fragments 8 and 9 reuse the rows of fragments 0 and
+            // 1) and leave as one 16-byte store per lane.
             const int hblk = c0 >> 5;
             constexpr int RB = 80;
-            static_assert(MT * RB <= NT * 48 && NT * 48 <= 2 * MT * 64, "h staging fits");
+            static_assert(MT * RB <= NT * 48 && NT * 48 <= 2 * MTX * 64, "h staging fits");
             uint8_t* R = wave == 0 ? a0 : wave == 1 ? a1 : wave == 2 ? w0 : w1;
 #pragma unroll
             for (int mf = 0; mf < MF; ++mf) {
@@ -664,7 +690,7 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                             const float gv = 16.f * acc[mf][f][i], uv = 16.f * acc[mf][2 + f][i];
                             const uint16_t hb = f32_to_bf16(gelu_tanh(gv) * uv);
                             s += bf16_to_f32(hb);
-                            *(uint16_t*)(R + r * RB + 2 * perm_pos(f * 16 + l16)) = hb;
+                            *(uint16_t*)(R + (r & (MT - 1)) * RB + 2 * perm_pos(f * 16 + l16)) = hb;
                         }
                         // sum over the 16 lanes holding this row's columns
                         s += dpp_mov_f32<DPP_QUAD_XOR1>(s);
@@ -674,7 +700,7 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                         if (ok && l16 == 0) hsum_out[(int64_t)hblk * hs_blk + p] = -1.5f * s;
                     }
                     const int r = mf * 16 + (lane >> 2), ch = lane & 3;
-                    const uint4 v = *(const uint4*)(R + r * RB + 16 * ch);
+                    const uint4 v = *(const uint4*)(R + (r & (MT - 1)) * RB + 16 * ch);
                     if (r < cnt) *(uint4*)(h_out + (int64_t)(base + r) * hpitch + hblk * 32 + 8 * ch) = v;
                 }
             }
@@ -687,7 +713,7 @@ __global__ __launch_bounds__(256) void ffn_mfma(
             // instead of 4 rows x 16 columns of 4-byte stores)
             const int H = ncols;
             constexpr int RS = 68;
-            static_assert(32 * RS * 4 <= NT * 48 && NT * 48 <= 2 * MT * 64, "y staging fits");
+            static_assert(32 * RS * 4 <= NT * 48 && NT * 48 <= 2 * MTX * 64, "y staging fits");
             float* R = reinterpret_cast<float*>(wave == 0 ? a0 : wave == 1 ? a1 : wave == 2 ? w0 : w1);
             const int cq = lane & 15;
 #pragma unroll
@@ -695,11 +721,12 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                 if (m2 < mfa) {
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
+                        if (m2 + h < MF)  // MF = 9: the last pair is one fragment
 #pragma unroll
-                        for (int nf = 0; nf < NF; ++nf)
+                            for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                R[(16 * h + 4 * g + i) * RS + 16 * nf + l16] = 16.f * acc[m2 + h][nf][i];
+                                for (int i = 0; i < 4; ++i)
+                                    R[(16 * h + 4 * g + i) * RS + 16 * nf + l16] = 16.f * acc[m2 + h][nf][i];
 #pragma unroll
                     for (int q = 0; q < 8; ++q) {
                         const int rl = 4 * q + (lane >> 4), r = 16 * m2 + rl;
@@ -722,8 +749,13 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         run(std::integral_constant<int, 4>{}, F4{});
     } else if (cnt <= 96) {
         run(std::integral_constant<int, 6>{}, F4{});
-    } else {
+    } else if (!BUF || cnt <= MT) {
         run(std::integral_constant<int, 8>{}, F4{});
+    } else if constexpr (BUF) {
+        if (cnt <= 144)
+            run(std::integral_constant<int, 9>{}, F4{});
+        else
+            run(std::integral_constant<int, MTX / 16>{}, F4{});
     }
 }
 

@@ -245,14 +245,17 @@ def test_mfma_tile_size_boundaries(I):
 
 @pytest.mark.parametrize("H,I", [(256, 512), (64, 64), (128, 192)])
 def test_mfma_tile_boundaries_among_many_experts(H, I):
-    # The slot counts above (1, 32, 33, 64, 65, 96, 97, 129) among 128 more
-    # experts of 384 slots each (three full tiles): the tile numbering and the
-    # XCD runs over a few hundred tiles, with every tile variant present.  The
-    # shapes give the two-stage ring 4, 1 and 2 block pairs (gate/up) and 8, 1
-    # and 3 (down), and leave waves without rows in the last column tile.
-    # Injected logits fix every token's expert; outputs are checked on the first
-    # and last token of the eight boundary experts and of a few others.
-    counts = [1, 32, 33, 64, 65, 96, 97, 129] + [384] * 128
+    # The slot counts above (1, 32, 33, 64, 65, 96, 97, 129) and the bounds of
+    # the merged last tile of up to 160 slots (144 and 145: one tile of 9 and
+    # of 10 fragments; 160: the largest single tile; 161: 128 + 33; 288:
+    # 128 + 160; 289: 128 + 128 + 33) among 128 more experts of 384 slots each
+    # (three full tiles): the tile numbering and the XCD runs over a few
+    # hundred tiles, with every tile variant present.  The shapes give the
+    # two-stage ring 4, 1 and 2 block pairs (gate/up) and 8, 1 and 3 (down),
+    # and leave waves without rows in the last column tile.  Injected logits
+    # fix every token's expert; outputs are checked on the first and last token
+    # of the fourteen boundary experts and of a few others.
+    counts = [1, 32, 33, 64, 65, 96, 97, 129, 144, 145, 160, 161, 288, 289] + [384] * 128
     T, E = sum(counts), len(counts)
     spec = synth.LayerSpec("tile-bounds-many-H%d-I%d" % (H, I), H=H, E=E, K=1, I=I, T=T, act="bf16",
                            router_std=1 / 16, seed=37)
@@ -261,8 +264,8 @@ def test_mfma_tile_boundaries_among_many_experts(H, I):
     owner = rng.permutation(np.repeat(np.arange(E), counts))
     lg = (rng.standard_normal((T, E)) * 0.1).astype(np.float32)
     lg[np.arange(T), owner] += 10.0
-    sample = np.concatenate([np.nonzero(owner == e)[0][[0, -1]] for e in range(8)] +
-                            [np.nonzero(owner == e)[0][[0, -1]] for e in (8, 70, E - 1)])
+    sample = np.concatenate([np.nonzero(owner == e)[0][[0, -1]] for e in range(14)] +
+                            [np.nonzero(owner == e)[0][[0, -1]] for e in (14, 70, E - 1)])
     g, res = _run(L, logits_in=lg, token_sample=np.unique(sample))
     assert np.array_equal(np.diff(g["offsets"]), np.array(counts))
 
