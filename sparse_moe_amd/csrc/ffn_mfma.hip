@@ -22,7 +22,8 @@
 // (rounded to bf16) the same way, so the down product reads it directly.
 //
 // Tiles: 128 slots x 256 weight rows per workgroup of 4 waves, each wave 128
-// slots x 64 rows (8 x 4 MFMA tiles); two Q4_0 blocks per stage.  For gate/up
+// slots x 64 rows (8 x 4 MFMA tiles); an expert's last tile may take up to 160
+// slots (10 x 4); two Q4_0 blocks per stage.  For gate/up
 // a wave's 64 rows are 32 gate rows and the 32 up rows of the same hidden
 // columns, so each lane holds gate and up of the same (slot, column) in
 // matching registers and GELU(g) * u is formed in the epilogue.
@@ -192,7 +193,9 @@ MOE_DEV void stage_products(const uint8_t* __restrict__ Sa, const float* __restr
 //  * Many workgroups (more than FFN_MFMA_LPT_UNITS): slot tiles in expert
 //    order, the sequence of workgroups cut into 8 equal runs, run x for XCD
 //    x, so the next slot tile of the same expert also shares the XCD's L2 (its
-//    weights).
+//    weights).  An expert's tiles hold MT slots each but the last, which takes
+//    up to mtx: a remainder of at most mtx - MT slots joins the tile before it
+//    instead of streaming the expert's weights once more for a few slots.
 //  * Few (a grid of about three rounds of resident workgroups or less, as with
 //    a few hundred tokens over many experts): how long the kernel takes is
 //    decided by how the tiles pack, and a tile's time grows with its slot
