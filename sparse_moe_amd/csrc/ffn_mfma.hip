@@ -529,6 +529,11 @@ __global__ __launch_bounds__(256) void ffn_mfma(
         // pair j: activations 128 bytes, block sums two blocks (2 cs_blk
         // floats) and weights 36 bytes further on
         const int cpair = 8 * cs_blk;
+        // A wave without weight rows (the last gate/up column tile when I is not
+        // a multiple of 128) still loads its share of the activations, which
+        // the other waves read, but not its weights, which nobody reads; the
+        // light ring keeps them, since its waits count every wave's loads alike.
+        const bool wload = LIGHT || active;
         auto issue = [&](const StageRef& S, int j) {
             if constexpr (BUF) {
 #pragma unroll
@@ -536,8 +541,10 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                 dma4(S.c + cdst, (uint32_t)cbyte, r_cs, (uint32_t)(cpair * j));
                 if (WIDE && wave == 0)
                     dma4(S.c + 2 * AROWS - 64, (uint32_t)cbyte_x, r_cs, (uint32_t)(cpair * j));
+                if (wload) {
 #pragma unroll
-                for (int i = 0; i < NWL; ++i) dma16(S.w + 64 * 48 * wave + 1024 * i, woff[i], r_w, 36u * j);
+                    for (int i = 0; i < NWL; ++i) dma16(S.w + 64 * 48 * wave + 1024 * i, woff[i], r_w, 36u * j);
+                }
             } else {
                 const uint8_t* act_b = reinterpret_cast<const uint8_t*>(act);
                 const uint8_t* cs_b = reinterpret_cast<const uint8_t*>(csum);
@@ -550,11 +557,13 @@ __global__ __launch_bounds__(256) void ffn_mfma(
                 if (WIDE && wave == 0)
                     __builtin_amdgcn_global_load_lds((glb_void_t*)(cs_b + cbyte_x + (int64_t)cpair * j),
                                                      (lds_void_t*)(S.c + 2 * AROWS - 64), 4, 0, 0);
+                if (wload) {
 #pragma unroll
-                for (int i = 0; i < NWL; ++i)
-                    __builtin_amdgcn_global_load_lds(
-                        (glb_void_t*)(We + woff[i] + 36u * (uint32_t)j),
-                        (lds_void_t*)(S.w + 64 * 48 * wave + 1024 * i), 16, 0, 0);
+                    for (int i = 0; i < NWL; ++i)
+                        __builtin_amdgcn_global_load_lds(
+                            (glb_void_t*)(We + woff[i] + 36u * (uint32_t)j),
+                            (lds_void_t*)(S.w + 64 * 48 * wave + 1024 * i), 16, 0, 0);
+                }
             }
         };
         const int swz = 16 * (g ^ ((l16 >> 2) & 3));  // this lane's chunk position in a row
