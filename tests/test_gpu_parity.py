@@ -55,7 +55,11 @@ def tile_covering_tokens(offsets: np.ndarray, sorted_slots: np.ndarray, K: int,
                          tile: int = 128) -> np.ndarray:
     """Tokens whose slots touch every (expert, slot tile) of the grouped GEMM:
     greedily, each uncovered tile contributes the token of its last slot (the
-    ragged end of a partial tile), which also covers that token's other slots."""
+    ragged end of a partial tile), which also covers that token's other slots.
+    The tiles are taken `tile` slots at a time, a finer cover than the kernel's
+    when it merges an expert's last few slots into a longer last tile: both
+    parts of such a tile (its first 128 slots and the rows past them) are then
+    sampled."""
     N = sorted_slots.size
     tile_of = np.empty(N, np.int64)
     tiles = []
